@@ -1,0 +1,112 @@
+"""FP8 E4M3 KV quantisation, from the format's definition (test-only).
+
+The format (froggydisk "LLM에서 KV 캐시는 얼마나 생길까", FP8 KV cache
+paragraph and format table): 1 sign, 4 exponent and 3 mantissa bits; the
+largest finite magnitude is 448; between 1 and 2 the values are 0.125 apart,
+between 2 and 4 they are 0.25 apart (so 3.14159 is stored as 3.25 and 0.1234
+as 0.125).  Values are divided by a scale before they are stored and
+multiplied by it when read.  Readings taken here:
+
+* Max 448 fixes the OCP "E4M3FN" variant: exponent bias 7, no infinities,
+  codes 0x7F and 0xFF are NaN, exponent field 0 is subnormal (2^-6 * m/8).
+* Encoding rounds to the nearest representable value, ties to the even
+  mantissa, and saturates magnitudes beyond 448 to 448.  The sign is kept
+  (-0 encodes as 0x80).
+* The page puts one scale per layer; here every (block, KV head) has its own
+  fp32 scale, separately for K and V: scale = absmax / 448 over the block's
+  filled rows, computed as an IEEE fp32 division, and y = x / scale also in
+  fp32 (the precision in which the integer code is decided).  An all-zero
+  block gets scale 0 and all-zero codes.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+BLOCK_SIZE = 16
+
+
+def decode_code(code: int) -> float:
+    """Value of one E4M3FN code, written out from the bit fields."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * 2.0 ** (e - 7) * (1.0 + m / 8.0)
+
+
+def decode_table() -> np.ndarray:
+    """float64 value of every code 0..255 (NaN for 0x7F and 0xFF)."""
+    return np.array([decode_code(c) for c in range(256)], dtype=np.float64)
+
+
+_POS = decode_table()[:0x7F]          # codes 0x00..0x7E: 0 .. 448, increasing
+
+
+def encode(y) -> np.ndarray:
+    """Nearest-even E4M3FN code of each fp32 value, saturating at +-448.
+
+    For each magnitude the two neighbouring representable values are looked up
+    in the sorted table of positive codes; the closer one wins, and on a tie
+    the code with an even mantissa (code LSB 0) wins.
+    """
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y.astype(np.float64))
+    hi = np.clip(np.searchsorted(_POS, a, side="left"), 1, len(_POS) - 1)
+    lo = hi - 1
+    dlo = a - _POS[lo]
+    dhi = _POS[hi] - a
+    tie_pick = np.where(lo % 2 == 0, lo, hi)
+    code = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, tie_pick))
+    code = np.where(_POS[hi] == a, hi, code)
+    code = np.where(a < E4M3_MAX, code, 0x7E)        # saturate (and +inf)
+    sign = np.signbit(y).astype(np.int64) << 7
+    return (code.astype(np.int64) | sign).astype(np.uint8)
+
+
+def block_scale(x_rows) -> np.float32:
+    """fp32 scale of one (block, head) tile: absmax over its filled rows / 448."""
+    x = np.asarray(x_rows, dtype=np.float32)
+    absmax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    return np.float32(absmax / np.float32(E4M3_MAX))
+
+
+def quantize_tile(x_rows, scale: np.float32) -> np.ndarray:
+    """Codes of one tile's filled rows under ``scale`` (y = x / scale in fp32)."""
+    x = np.asarray(x_rows, dtype=np.float32)
+    if scale == 0:
+        return np.zeros(x.shape, dtype=np.uint8)
+    return encode(x / np.float32(scale))
+
+
+def quantize_sequence(X: np.ndarray):
+    """Quantise one sequence's logical K (or V) ``[s][n_kv][d]``.
+
+    Logical block ``b`` (tokens 16b .. 16b+15, the last one possibly short) of
+    KV head ``j`` gets one scale.  Returns codes ``[s][n_kv][d]`` (uint8) and
+    scales ``[n_blocks][n_kv]`` (float32).
+    """
+    X = np.asarray(X, dtype=np.float32)
+    s, n_kv, d = X.shape
+    nb = -(-s // BLOCK_SIZE)
+    codes = np.zeros((s, n_kv, d), dtype=np.uint8)
+    scales = np.zeros((nb, n_kv), dtype=np.float32)
+    for b in range(nb):
+        lo, hi = b * BLOCK_SIZE, min(s, (b + 1) * BLOCK_SIZE)
+        for j in range(n_kv):
+            sc = block_scale(X[lo:hi, j, :])
+            scales[b, j] = sc
+            codes[lo:hi, j, :] = quantize_tile(X[lo:hi, j, :], sc)
+    return codes, scales
+
+
+def dequantize_sequence(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """float64 K^ (or V^) = decoded code times its block's scale."""
+    table = decode_table()
+    s = codes.shape[0]
+    blk = np.arange(s) // BLOCK_SIZE
+    return table[codes] * scales[blk, :].astype(np.float64)[:, :, None]

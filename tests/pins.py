@@ -1,0 +1,376 @@
+"""Checks that pin the oracle to facts outside itself.
+
+Each function returns the worst deviation (or a bool) of one oracle part
+against an independent source: a value the pages print, a closed form, a
+library routine, or brute force.  The oracle tests assert on them; the
+mutation tests plant plausible mistakes in the oracle and assert that at
+least one of them notices.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+from oracle import attention, e4m3, footprint, numerics, paged, scores
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- footprint
+def footprint_mismatches() -> list:
+    g = _golden("kv_bytes_per_token.json")
+    bad = []
+    for row in g["per_token"]:
+        got = footprint.kv_bytes_per_token(row["layers"], row["n_kv"], row["head_dim"],
+                                           row["bytes_per_elem"])
+        if got != row["bytes"] or got / 1024 != row["kib"]:
+            bad.append(("per_token", row["model"], got))
+    for row in g["per_request_gib"]:
+        for key, (L, nkv, d) in (("8b", (32, 8, 128)), ("70b", (80, 8, 128))):
+            gib = footprint.request_kv_bytes(row["tokens"], L, nkv, d, 2) / 2 ** 30
+            if abs(gib - row[key]) > 0.005 + 1e-12:      # the page prints two decimals
+                bad.append(("per_request", key, row["tokens"], gib))
+    r = g["review_70b"]
+    bpt = footprint.kv_bytes_per_token(80, 8, 128, 2)
+    if round(bpt / 1e6, 2) != r["mb_per_token_decimal"]:
+        bad.append(("mb", bpt))
+    if round(footprint.request_kv_bytes(128_000, 80, 8, 128, 2) / 1e9, 1) != r["gb_at_128000"]:
+        bad.append(("gb128k",))
+    if round(footprint.request_kv_bytes(512_000, 80, 8, 128, 2) / 1e9, 1) != r["gb_at_512000"]:
+        bad.append(("gb512k",))
+    it = _golden("intensity.json")
+    for c in it["cases"]:
+        got = footprint.long_context_intensity(c["n_q"], c["n_kv"], c["bytes_per_elem"])
+        if got != c["flop_per_byte"]:
+            bad.append(("intensity", c, got))
+    if round(it["h100_ridge"] / footprint.long_context_intensity(64, 8, 0.25), 1) != it["ratio_2bit_to_ridge"]:
+        bad.append(("ridge",))
+    return bad
+
+
+# ---------------------------------------------------------------- bf16
+def bf16_rounding_mismatches(n=200_000, seed=0) -> int:
+    """Oracle's nearest-even bf16 rounding against torch's fp32 -> bf16 cast."""
+    import torch
+    rng = np.random.default_rng(seed)
+    x = np.concatenate([
+        rng.standard_normal(n).astype(np.float32),
+        (rng.standard_normal(n) * 1e-38).astype(np.float32),     # subnormal range
+        (rng.standard_normal(n) * 1e37).astype(np.float32),
+        # exact ties: bf16 values plus half a quantum
+        (numerics.bf16_bits_to_f64(rng.integers(0x0080, 0x7F00, n).astype(np.uint16))
+         * (1 + 2.0 ** -8)).astype(np.float32),
+    ])
+    ours = numerics.f64_to_bf16_bits(x.astype(np.float64))
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return int(np.count_nonzero(ours != theirs))
+
+
+# ---------------------------------------------------------------- e4m3
+def e4m3_decode_mismatches() -> int:
+    """Decode of all 256 codes against torch.float8_e4m3fn -> float32."""
+    import torch
+    theirs = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float32)
+    theirs = theirs.double().numpy()
+    ours = e4m3.decode_table()
+    both_nan = np.isnan(ours) & np.isnan(theirs)
+    same = both_nan | ((ours == theirs) & (np.signbit(ours) == np.signbit(theirs)))
+    return int(np.count_nonzero(~same))
+
+
+def e4m3_encode_mismatches(n=200_000, seed=1) -> int:
+    """Encode against torch's nearest-even cast, inside +-464 where torch does not overflow."""
+    import torch
+    rng = np.random.default_rng(seed)
+    table = e4m3.decode_table()
+    fin = table[np.isfinite(table)]
+    mids = []
+    s = np.sort(np.unique(fin))
+    mids = (s[1:] + s[:-1]) / 2                   # exact ties in fp32
+    x = np.concatenate([
+        (rng.uniform(-463, 463, n)).astype(np.float32),
+        (rng.standard_normal(n) * 2.0 ** rng.integers(-12, 6, n)).astype(np.float32),
+        mids.astype(np.float32), fin.astype(np.float32),
+    ])
+    ours = e4m3.encode(x)
+    theirs = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return int(np.count_nonzero(ours != theirs))
+
+
+def e4m3_page_fact_failures() -> list:
+    g = _golden("e4m3_facts.json")
+    t = e4m3.decode_table()
+    bad = []
+    fin = t[np.isfinite(t)]
+    if np.max(fin) != g["max_finite"]:
+        bad.append("max")
+    if e4m3.encode(np.array([1e6], np.float32))[0] != e4m3.encode(np.array([448.0], np.float32))[0]:
+        bad.append("saturate")
+    for sp in g["spacing"]:
+        v = np.sort(fin[(fin >= sp["lo"]) & (fin <= sp["hi"])])
+        if not np.all(np.diff(v) == sp["step"]):
+            bad.append(("spacing", sp))
+    for ex in g["examples"]:
+        c = e4m3.encode(np.array([ex["in"]], np.float32))[0]
+        if t[c] != ex["stored"]:
+            bad.append(("example", ex, t[c]))
+    b = g["bits"]
+    if 2 ** (b["sign"] + b["exponent"] + b["mantissa"]) != len(t):
+        bad.append("bits")
+    return bad
+
+
+# ---------------------------------------------------------------- attention
+def sdpa_max_error(seed=0) -> float:
+    """Oracle decode output against torch scaled_dot_product_attention (float64, GQA)."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for (n_q, n_kv, d, s) in [(4, 1, 64, 37), (8, 2, 16, 5), (32, 8, 128, 70), (8, 8, 32, 1),
+                              (64, 8, 128, 33), (6, 3, 8, 19)]:
+        q = rng.standard_normal((n_q, d))
+        K = rng.standard_normal((s, n_kv, d)) * 1.7
+        V = rng.standard_normal((s, n_kv, d))
+        o, _ = attention.decode_sequence(q, K, V)
+        tq = torch.from_numpy(q)[None, :, None, :]
+        tk = torch.from_numpy(K).permute(1, 0, 2)[None]
+        tv = torch.from_numpy(V).permute(1, 0, 2)[None]
+        ref = F.scaled_dot_product_attention(tq, tk, tv, enable_gqa=True)[0, :, 0, :].numpy()
+        worst = max(worst, float(np.max(np.abs(o - ref))))
+    return worst
+
+
+def brute_force_max_error(seed=1) -> float:
+    """Oracle (o, lse) against explicit pure-Python loops on tiny inputs."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for (n_q, n_kv, d, s) in [(2, 1, 3, 4), (4, 2, 5, 7), (3, 3, 2, 1), (8, 2, 4, 6)]:
+        q = rng.standard_normal((n_q, d))
+        K = rng.standard_normal((s, n_kv, d))
+        V = rng.standard_normal((s, n_kv, d))
+        o, lse = attention.decode_sequence(q, K, V)
+        g = n_q // n_kv
+        for h in range(n_q):
+            j = h // g
+            ls = [sum(q[h][c] * K[t][j][c] for c in range(d)) / math.sqrt(d) for t in range(s)]
+            den = math.fsum(math.exp(x) for x in ls)
+            for c in range(d):
+                num = math.fsum(math.exp(ls[t]) * V[t][j][c] for t in range(s))
+                worst = max(worst, abs(num / den - o[h][c]))
+            worst = max(worst, abs(math.log(den) - lse[h]))
+    return worst
+
+
+def lse_library_max_error(seed=2) -> float:
+    """lse against scipy's logsumexp of logits computed by torch matmul."""
+    import torch
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for (n_q, n_kv, d, s) in [(8, 2, 64, 300), (4, 4, 128, 9)]:
+        q = rng.standard_normal((n_q, d)) * 3
+        K = rng.standard_normal((s, n_kv, d))
+        V = rng.standard_normal((s, n_kv, d))
+        _, lse = attention.decode_sequence(q, K, V)
+        tq = torch.from_numpy(q)
+        tk = torch.from_numpy(K).repeat_interleave(n_q // n_kv, dim=1)   # [s][n_q][d]
+        lg = torch.einsum("hd,shd->hs", tq, tk).numpy() / np.sqrt(d)
+        worst = max(worst, float(np.max(np.abs(lse - logsumexp(lg, axis=1)))))
+    return worst
+
+
+def split_merge_max_error(seed=3) -> float:
+    """Merging any chunking's partials reproduces the unsplit result."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((8, 32))
+    K = rng.standard_normal((203, 2, 32)) * 2
+    V = rng.standard_normal((203, 2, 32))
+    o, lse = attention.decode_sequence(q, K, V)
+    worst = 0.0
+    for chunk in (1, 16, 48, 100, 203, 512):
+        oc, lc = attention.chunk_partials(q, K, V, chunk)
+        om, lm = attention.merge_partials(oc, lc)
+        worst = max(worst, float(np.max(np.abs(om - o))), float(np.max(np.abs(lm - lse))))
+    return worst
+
+
+def special_case_failures(seed=4) -> list:
+    rng = np.random.default_rng(seed)
+    bad = []
+    d = 16
+    q = rng.standard_normal((4, d))
+    # s = 1: output is V_0 exactly, lse = l_0
+    K = rng.standard_normal((1, 2, d))
+    V = rng.standard_normal((1, 2, d))
+    o, lse = attention.decode_sequence(q, K, V)
+    for h in range(4):
+        if not np.array_equal(o[h], V[0, h // 2]):
+            bad.append("s1")
+    # q = 0: uniform weights, o = mean of V, lse = log s
+    K = rng.standard_normal((10, 2, d))
+    V = rng.standard_normal((10, 2, d))
+    o, lse = attention.decode_sequence(np.zeros((4, d)), K, V)
+    if np.max(np.abs(o[0] - V[:, 0].mean(0))) > 1e-14 or abs(lse[0] - math.log(10)) > 1e-14:
+        bad.append("q0")
+    # constant V: output equals the constant
+    Vc = np.full((10, 2, d), 0.375)
+    o, _ = attention.decode_sequence(q, K, Vc)
+    if np.max(np.abs(o - 0.375)) > 1e-15:
+        bad.append("constV")
+    # one logit far above the rest: output is that token's V
+    K = np.zeros((10, 2, d))
+    K[7, :, :] = q[0] / np.linalg.norm(q[0]) * 400.0
+    o, _ = attention.decode_sequence(q[:1].repeat(4, 0), K, V)
+    if np.max(np.abs(o[0] - V[7, 0])) > 1e-12:
+        bad.append("dominant")
+    # empty context
+    o, lse = attention.decode_sequence(q, np.zeros((0, 2, d)), np.zeros((0, 2, d)))
+    if np.any(o != 0) or np.any(lse != -np.inf):
+        bad.append("empty")
+    # weights sum to one
+    a = attention.attention_weights_sequence(q, rng.standard_normal((50, 2, d)) * 3)
+    if np.max(np.abs(a.sum(1) - 1)) > 1e-12:
+        bad.append("sum1")
+    return bad
+
+
+# ---------------------------------------------------------------- paging
+def block_table_example_failures() -> list:
+    g = _golden("block_table_example.json")
+    bs = g["block_size"]
+    bad = []
+    used = sorted(b for t in g["tables"].values() for b in t)
+    if used != list(range(g["pool_blocks"])):
+        bad.append("cover")
+    lay = paged.PoolLayout(num_layers=1, num_blocks=g["pool_blocks"], n_kv=2, head_dim=4)
+    pool = np.full(lay.total_elems, np.nan)
+    rng = np.random.default_rng(5)
+    data = {}
+    for name, table in g["tables"].items():
+        s = len(table) * bs - (3 if name != "A" else 0)     # the last block may be partial
+        if paged.tail_waste(s) > g["max_waste_tokens"]:
+            bad.append(("waste", name))
+        K = rng.standard_normal((s, 2, 4))
+        V = rng.standard_normal((s, 2, 4))
+        paged.scatter(pool, lay, 0, table, K, V)
+        data[name] = (table, K, V)
+        # the slot of token t lies in physical block table[t // 16] at row t % 16
+        for t in range(s):
+            p, row = divmod(paged.slot(table, t), bs)
+            if p != table[t // bs] or row != t % bs:
+                bad.append(("slot", name, t))
+    for name, (table, K, V) in data.items():
+        K2, V2 = paged.gather(pool, lay, 0, table, K.shape[0])
+        if not (np.array_equal(K, K2) and np.array_equal(V, V2)):
+            bad.append(("roundtrip", name))
+    # documented layout: K token-major, V channel-major inside a tile pair
+    if lay.k_offset(0, 3, 1, 2, 1) - lay.tile_base(0, 3, 1) != 2 * 4 + 1:
+        bad.append("k_layout")
+    if lay.v_offset(0, 3, 1, 2, 1) - lay.tile_base(0, 3, 1) != 16 * 4 + 1 * 16 + 2:
+        bad.append("v_layout")
+    return bad
+
+
+def placement_invariance_max_error(seed=6) -> float:
+    """Paged result (gather through any block table) equals the contiguous result."""
+    rng = np.random.default_rng(seed)
+    s, n_kv, d, n_q = 75, 2, 8, 4
+    K = rng.standard_normal((s, n_kv, d))
+    V = rng.standard_normal((s, n_kv, d))
+    q = rng.standard_normal((n_q, d))
+    o_ref, lse_ref = attention.decode_sequence(q, K, V)
+    worst = 0.0
+    nb = paged.blocks_needed(s)
+    for trial in range(3):
+        lay = paged.PoolLayout(1, 12, n_kv, d)
+        table = rng.permutation(12)[:nb]
+        pool = np.zeros(lay.total_elems)
+        paged.scatter(pool, lay, 0, table, K, V)
+        K2, V2 = paged.gather(pool, lay, 0, table, s)
+        o, lse = attention.decode_sequence(q, K2, V2)
+        worst = max(worst, float(np.max(np.abs(o - o_ref))), float(np.max(np.abs(lse - lse_ref))))
+    return worst
+
+
+# ---------------------------------------------------------------- scores
+def score_failures(seed=7) -> list:
+    rng = np.random.default_rng(seed)
+    bad = []
+    d, n_q, n_kv, s, L = 16, 8, 2, 40, 3
+    alphas = []
+    for _ in range(L):
+        q = rng.standard_normal((n_q, d))
+        K = rng.standard_normal((s, n_kv, d)) * 2
+        alphas.append(attention.attention_weights_sequence(q, K))
+    inc = scores.step_increment(alphas)
+    if abs(inc.sum() - 1.0) > 1e-12:
+        bad.append("sum1")
+    # per-layer calls with weight 1/L add up to the step increment
+    acc = sum(scores.layer_increment(a, 1.0 / L) for a in alphas)
+    if np.max(np.abs(acc - inc)) > 1e-15:
+        bad.append("layers")
+    # uniform attention: every position gains 1/s
+    a0 = attention.attention_weights_sequence(np.zeros((n_q, d)), rng.standard_normal((s, n_kv, d)))
+    if np.max(np.abs(scores.step_increment([a0]) - 1.0 / s)) > 1e-15:
+        bad.append("uniform")
+    # brute force: one layer, explicit double loop
+    a = alphas[0]
+    for t in range(s):
+        bf = math.fsum(a[h][t] for h in range(n_q)) / n_q
+        if abs(bf - scores.step_increment([a])[t]) > 1e-15:
+            bad.append(("bf", t))
+            break
+    return bad
+
+
+# ---------------------------------------------------------------- fp8 path
+def fp8_quant_failures(seed=8) -> list:
+    rng = np.random.default_rng(seed)
+    bad = []
+    s, n_kv, d = 37, 2, 8                       # last block has 5 rows
+    X = (rng.standard_normal((s, n_kv, d)) * 3).astype(np.float32)
+    X[16:32, 1, :] = 0                          # an all-zero block
+    codes, sc = e4m3.quantize_sequence(X)
+    table = e4m3.decode_table()
+    for b in range(3):
+        for j in range(n_kv):
+            rows = X[b * 16:min(s, b * 16 + 16), j]
+            am = np.float32(np.max(np.abs(rows)))
+            if sc[b, j] != np.float32(am / np.float32(448)):
+                bad.append(("scale", b, j))
+            c = codes[b * 16:min(s, b * 16 + 16), j]
+            if am == 0:
+                if np.any(c != 0):
+                    bad.append("zero_block")
+                continue
+            # the element holding the absmax maps to +-448 exactly
+            if np.max(np.abs(table[c])) != 448.0:
+                bad.append(("max448", b, j))
+    # a tile's scale ignores rows past the sequence end (the short last block)
+    X2 = X.copy()
+    Xext = np.concatenate([X2, np.full((11, n_kv, d), 1e30, np.float32)])
+    c2, sc2 = e4m3.quantize_sequence(Xext[:s])
+    if not (np.array_equal(c2, codes) and np.array_equal(sc2, sc)):
+        bad.append("tail")
+    # dequantised values are within half a step of the input
+    deq = e4m3.dequantize_sequence(codes, sc)
+    rel = np.abs(deq - X) / np.maximum(np.abs(X), 1e-30)
+    big = np.abs(X) >= 2 ** -6 * np.repeat(sc, 16, axis=0)[:s, :, None]
+    if np.max(rel[big]) > 2.0 ** -4 + 1e-7:
+        bad.append("halfstep")
+    # power-of-two scale and values on the grid: exact round trip
+    Y = np.zeros((1, 1, 4), np.float32)
+    Y[0, 0] = [448.0, -3.25, 0.125, 2 ** -9]
+    cY, sY = e4m3.quantize_sequence(Y)
+    if sY[0, 0] != 1.0 or not np.array_equal(e4m3.dequantize_sequence(cY, sY)[0, 0], Y[0, 0]):
+        bad.append("exact")
+    return bad

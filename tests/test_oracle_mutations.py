@@ -1,0 +1,138 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check a pin notices.
+
+Each case patches one oracle function with a wrong variant -- a dropped term,
+a wrong sign or index, a transposed operand, a wrong constant -- and asserts
+that at least one of the pins in ``pins.py`` fails.  The patch is undone after
+every case.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import pins
+from oracle import attention, e4m3, footprint, paged, scores
+
+
+def _all_pins_pass() -> bool:
+    return (pins.footprint_mismatches() == []
+            and pins.e4m3_decode_mismatches() == 0
+            and pins.e4m3_encode_mismatches(n=20_000) == 0
+            and pins.e4m3_page_fact_failures() == []
+            and pins.sdpa_max_error() < 1e-13
+            and pins.brute_force_max_error() < 1e-13
+            and pins.lse_library_max_error() < 1e-12
+            and pins.split_merge_max_error() < 1e-12
+            and pins.special_case_failures() == []
+            and pins.block_table_example_failures() == []
+            and pins.placement_invariance_max_error() == 0.0
+            and pins.score_failures() == []
+            and pins.fp8_quant_failures() == [])
+
+
+def _modulo_heads(h, n_q, n_kv):
+    return h % n_kv
+
+
+def _no_scale_logits(q_h, K_j):
+    return K_j @ q_h
+
+
+def _natural_scale_logits(q_h, K_j):
+    return (K_j @ q_h) / q_h.shape[-1]
+
+
+def _lse_without_max(q_h, K_j, V_j):
+    s, d = K_j.shape
+    if s == 0:
+        return np.zeros(d), -np.inf
+    l = attention.logits(q_h, K_j)
+    alpha, m, Z = attention.softmax_weights(l)
+    return alpha @ V_j, math.log(Z)
+
+
+def _merge_unweighted(o_c, lse_c):
+    lead = o_c.shape[:-2]
+    o = o_c.mean(axis=-2)
+    M = np.max(lse_c, axis=-1)
+    return o.reshape(*lead, o_c.shape[-1]), M
+
+
+def _decode_code_bias8(code):
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -7
+    return sign * 2.0 ** (e - 8) * (1.0 + m / 8.0)
+
+
+def _encode_ties_away(y):
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y.astype(np.float64))
+    P = e4m3._POS
+    hi = np.clip(np.searchsorted(P, a, side="left"), 1, len(P) - 1)
+    lo = hi - 1
+    code = np.where(a - P[lo] < P[hi] - a, lo, hi)
+    code = np.where(a < 448.0, code, 0x7E)
+    return (code | (np.signbit(y).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def _bytes_no_factor2(layers, n_kv, head_dim, w):
+    return layers * n_kv * head_dim * w
+
+
+def _v_token_major(self, layer, block, head, row, ch):
+    return self.tile_base(layer, block, head) + 16 * self.head_dim + row * self.head_dim + ch
+
+
+def _slot_off_by_one(table_row, t):
+    return int(table_row[t // 16]) * 16 + (t + 1) % 16
+
+
+def _layer_inc_no_head_mean(alpha, weight):
+    return weight * alpha.sum(axis=0)
+
+
+def _step_inc_no_head_mean(alphas):
+    acc = np.zeros(alphas[0].shape[1])
+    for a in alphas:
+        acc += a.sum(axis=0)
+    return acc / len(alphas)
+
+
+def _scale_over_256(x_rows):
+    x = np.asarray(x_rows, dtype=np.float32)
+    return np.float32(np.float32(np.max(np.abs(x))) / np.float32(256.0))
+
+
+MUTATIONS = [
+    ("heads modulo instead of grouped", attention, "head_group", _modulo_heads),
+    ("logit scale dropped", attention, "logits", _no_scale_logits),
+    ("logit scale 1/d", attention, "logits", _natural_scale_logits),
+    ("lse without max", attention, "decode_head", _lse_without_max),
+    ("merge ignores lse", attention, "merge_partials", _merge_unweighted),
+    ("e4m3 bias 8", e4m3, "decode_code", _decode_code_bias8),
+    ("e4m3 ties away", e4m3, "encode", _encode_ties_away),
+    ("bytes/token missing K+V factor", footprint, "kv_bytes_per_token", _bytes_no_factor2),
+    ("V stored token-major", paged.PoolLayout, "v_offset", _v_token_major),
+    ("slot off by one", paged, "slot", _slot_off_by_one),
+    ("score missing head mean", scores, "layer_increment", _layer_inc_no_head_mean),
+    ("score step missing head mean", scores, "step_increment", _step_inc_no_head_mean),
+    ("fp8 scale absmax/256", e4m3, "block_scale", _scale_over_256),
+]
+
+
+def test_unpatched_oracle_passes_every_pin():
+    assert _all_pins_pass()
+
+
+@pytest.mark.parametrize("name,mod,attr,bad", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, mod, attr, bad):
+    monkeypatch.setattr(mod, attr, bad)
+    if mod is e4m3 and attr == "decode_code":
+        monkeypatch.setattr(e4m3, "_POS", np.array([bad(c) for c in range(0x7F)]))
+    assert not _all_pins_pass(), f"no pin caught: {name}"
