@@ -1,0 +1,247 @@
+"""Python binding of libkvdecode (paged GQA decode attention for MI355X).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of ``libkvdecode.so``.  PyTorch supplies device memory and streams.
+The functions keep the C names; see ``include/kvdecode.h`` for the layout,
+ownership and error rules.  Importing this package fails if the library has
+not been built (``python -m decode_attention_paged_04_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvdecode.so")
+
+BLOCK_SIZE = 16
+KVD_BF16, KVD_FP8_E4M3 = 0, 1
+STATUS = {0: "KVD_OK", 1: "KVD_ERR_INVALID_ARG", 2: "KVD_ERR_UNSUPPORTED", 3: "KVD_ERR_DTYPE",
+          4: "KVD_ERR_WORKSPACE", 5: "KVD_ERR_HIP"}
+
+
+class KvdError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("n_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int32), ("n_q", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("context_lens", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("lse_out", ctypes.c_void_p), ("chunk_tokens", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("score", ctypes.c_void_p), ("score_stride", ctypes.c_int32),
+                ("score_weight", ctypes.c_float)]
+
+
+EXPORTS = {
+    "kvd_pool_bytes": (ctypes.POINTER(PoolDesc), ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)),
+    "kvd_create_pool": (ctypes.POINTER(PoolDesc), ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)),
+    "kvd_destroy_pool": (ctypes.c_void_p,),
+    "kvd_write_kv": (ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                     ctypes.c_int32, ctypes.c_void_p),
+    "kvd_decode_plan": (ctypes.c_void_p, ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_int32),
+                        ctypes.POINTER(ctypes.c_int32)),
+    "kvd_decode_workspace_bytes": (ctypes.c_void_p, ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)),
+    "kvd_decode_attn": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs), ctypes.c_void_p),
+    "kvd_decode_attn_fp8": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs), ctypes.c_void_p),
+    "kvd_merge_partials": (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p),
+    "kvd_status_string": (ctypes.c_int,),
+    "kvd_debug_gather_offsets": (ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p),
+    "kvd_debug_fp8_decode": (ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m decode_attention_paged_04_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, argtypes in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = list(argtypes)
+        fn.restype = ctypes.c_char_p if name == "kvd_status_string" else ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise KvdError(st, where)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    if torch.cuda.is_available():
+        return int(torch.cuda.current_stream().cuda_stream)
+    return None
+
+
+def kvd_pool_bytes(num_layers: int, num_blocks: int, n_kv: int, head_dim: int,
+                   dtype: int = KVD_BF16, block_size: int = BLOCK_SIZE):
+    d = PoolDesc(num_layers, num_blocks, block_size, n_kv, head_dim, dtype)
+    kv, sc = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib.kvd_pool_bytes(ctypes.byref(d), ctypes.byref(kv), ctypes.byref(sc)), "kvd_pool_bytes")
+    return kv.value, sc.value
+
+
+class Pool:
+    """Host handle over a caller-owned pool (``kv`` and, for FP8, ``scales``)."""
+
+    def __init__(self, desc: PoolDesc, kv, scales, handle: int):
+        self.desc, self.kv, self.scales, self.handle = desc, kv, scales, handle
+
+    @property
+    def fp8(self) -> bool:
+        return self.desc.dtype == KVD_FP8_E4M3
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            lib.kvd_destroy_pool(h)
+            self.handle = None
+
+
+def kvd_create_pool(num_layers: int, num_blocks: int, n_kv: int, head_dim: int, kv, scales=None,
+                    dtype: int = KVD_BF16, block_size: int = BLOCK_SIZE) -> Pool:
+    """Wrap device buffers ``kv`` (and ``scales`` for FP8) as a pool."""
+    d = PoolDesc(num_layers, num_blocks, block_size, n_kv, head_dim, dtype)
+    h = ctypes.c_void_p(0)
+    _check(lib.kvd_create_pool(ctypes.byref(d), _ptr(kv), _ptr(scales), ctypes.byref(h)), "kvd_create_pool")
+    return Pool(d, kv, scales, h.value)
+
+
+def allocate_pool(num_layers: int, num_blocks: int, n_kv: int, head_dim: int,
+                  dtype: int = KVD_BF16, device="cuda") -> Pool:
+    """Allocate the pool's memory with torch and create the handle."""
+    import torch
+    kv_bytes, sc_bytes = kvd_pool_bytes(num_layers, num_blocks, n_kv, head_dim, dtype)
+    kv = torch.empty(kv_bytes, dtype=torch.uint8, device=device)
+    sc = torch.zeros(sc_bytes // 4, dtype=torch.float32, device=device) if sc_bytes else None
+    return kvd_create_pool(num_layers, num_blocks, n_kv, head_dim, kv, sc, dtype)
+
+
+def kvd_write_kv(pool: Pool, layer: int, k, v, slot_mapping, stream=None):
+    """Store bf16 ``k``/``v`` ``[n_tok][n_kv][head_dim]`` at ``slot_mapping`` (int32)."""
+    n = int(slot_mapping.numel())
+    _check(lib.kvd_write_kv(pool.handle, layer, _ptr(k), _ptr(v), _ptr(slot_mapping), n, _stream(stream)),
+           "kvd_write_kv")
+
+
+def slot_mapping_for(block_table, context_lens):
+    """Caller-side helper: slots of every token of every sequence, packed in order.
+
+    Token t of sequence i goes to ``block_table[i][t // 16] * 16 + t % 16``
+    (the write call's slot convention).  Works on CPU or device tensors.
+    """
+    import torch
+    bt = block_table.to(torch.int64)
+    lens = context_lens.to(torch.int64).cpu().tolist()
+    parts = []
+    for i, s in enumerate(lens):
+        t = torch.arange(s, device=bt.device)
+        parts.append(bt[i, t // BLOCK_SIZE] * BLOCK_SIZE + t % BLOCK_SIZE)
+    if not parts:
+        return torch.zeros(0, dtype=torch.int32, device=bt.device)
+    return torch.cat(parts).to(torch.int32)
+
+
+def make_args(q, block_table, context_lens, max_context_len: int, out, lse_out=None,
+              chunk_tokens: int = 0, workspace=None, score=None, score_weight: float = 0.0,
+              n_q: Optional[int] = None) -> DecodeArgs:
+    b = int(block_table.shape[0])
+    return DecodeArgs(
+        b, int(n_q if n_q is not None else q.shape[1]), int(block_table.shape[1]), int(max_context_len),
+        _ptr(q), _ptr(block_table), _ptr(context_lens), _ptr(out), _ptr(lse_out), int(chunk_tokens),
+        _ptr(workspace), int(workspace.numel() * workspace.element_size()) if workspace is not None else 0,
+        _ptr(score), int(score.shape[1]) if score is not None else 0, float(score_weight))
+
+
+def kvd_decode_plan(pool: Pool, args: DecodeArgs):
+    c, n = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib.kvd_decode_plan(pool.handle, ctypes.byref(args), ctypes.byref(c), ctypes.byref(n)),
+           "kvd_decode_plan")
+    return c.value, n.value
+
+
+def kvd_decode_workspace_bytes(pool: Pool, args: DecodeArgs) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.kvd_decode_workspace_bytes(pool.handle, ctypes.byref(args), ctypes.byref(n)),
+           "kvd_decode_workspace_bytes")
+    return n.value
+
+
+def allocate_workspace(pool: Pool, args: DecodeArgs, device="cuda"):
+    import torch
+    n = kvd_decode_workspace_bytes(pool, args)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device) if n else None
+    if ws is not None:
+        args.workspace, args.workspace_bytes = _ptr(ws), n
+    return ws
+
+
+def kvd_decode_attn(pool: Pool, layer: int, args: DecodeArgs, stream=None):
+    _check(lib.kvd_decode_attn(pool.handle, layer, ctypes.byref(args), _stream(stream)), "kvd_decode_attn")
+
+
+def kvd_decode_attn_fp8(pool: Pool, layer: int, args: DecodeArgs, stream=None):
+    _check(lib.kvd_decode_attn_fp8(pool.handle, layer, ctypes.byref(args), _stream(stream)),
+           "kvd_decode_attn_fp8")
+
+
+def kvd_merge_partials(part_o, part_lse, out, lse_out=None, stream=None):
+    """part_o fp32 ``[b][n_q][n_chunks][d]``, part_lse ``[b][n_q][n_chunks]`` -> out bf16."""
+    b, n_q, nc, d = (int(x) for x in part_o.shape)
+    _check(lib.kvd_merge_partials(_ptr(part_o), _ptr(part_lse), b, n_q, nc, d, _ptr(out), _ptr(lse_out),
+                                  _stream(stream)), "kvd_merge_partials")
+
+
+def kvd_status_string(status: int) -> str:
+    return lib.kvd_status_string(status).decode()
+
+
+def kvd_debug_gather_offsets(pool: Pool, layer: int, block_table, n_tok: int, out_k, out_v, stream=None):
+    b, mb = (int(x) for x in block_table.shape)
+    _check(lib.kvd_debug_gather_offsets(pool.handle, layer, _ptr(block_table), mb, b, n_tok, _ptr(out_k),
+                                        _ptr(out_v), _stream(stream)), "kvd_debug_gather_offsets")
+
+
+def kvd_debug_fp8_decode(codes, out, stream=None):
+    _check(lib.kvd_debug_fp8_decode(_ptr(codes), int(codes.numel()), _ptr(out), _stream(stream)),
+           "kvd_debug_fp8_decode")
+
+
+def decode(pool: Pool, layer: int, q, block_table, context_lens, max_context_len: int, out=None,
+           lse_out=None, chunk_tokens: int = 0, score=None, score_weight: float = 0.0,
+           workspace=None, stream=None):
+    """Convenience: allocate out/workspace as needed and run one decode call."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    args = make_args(q, block_table, context_lens, max_context_len, out, lse_out, chunk_tokens,
+                     workspace, score, score_weight)
+    ws = workspace
+    if ws is None:
+        ws = allocate_workspace(pool, args, device=q.device)
+    (kvd_decode_attn_fp8 if pool.fp8 else kvd_decode_attn)(pool, layer, args, stream)
+    return out, ws

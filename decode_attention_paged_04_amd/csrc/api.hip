@@ -1,0 +1,277 @@
+// C ABI of libkvdecode: validation, pool layout, launch planning, workspace.
+#include <new>
+
+#include "kvd_internal.h"
+
+struct kvd_pool {
+  kvd::PoolView v;
+};
+
+namespace {
+
+using kvd::DecodePlan;
+using kvd::PoolView;
+
+// Auto split: aim for about this many (sequence, KV head, chunk) workgroups
+// per launch -- several per compute unit on a 256-CU part -- with chunks no
+// shorter than kMinChunk tokens.
+constexpr int64_t kTargetWorkgroups = 1024;
+constexpr int32_t kMinChunk = 256;
+constexpr int32_t kChunkQuantum = 128;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+kvd_status check_desc(const kvd_pool_desc* d) {
+  if (!d) return KVD_ERR_INVALID_ARG;
+  if (d->num_layers < 1 || d->num_blocks < 1 || d->n_kv < 1) return KVD_ERR_INVALID_ARG;
+  if (d->dtype != KVD_BF16 && d->dtype != KVD_FP8_E4M3) return KVD_ERR_INVALID_ARG;
+  if (d->block_size != kvd::kBlock) return KVD_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return KVD_ERR_UNSUPPORTED;
+  const int64_t eb = d->dtype == KVD_BF16 ? 2 : 1;
+  const int64_t layer = (int64_t)d->num_blocks * d->n_kv * 2 * kvd::kBlock * d->head_dim * eb;
+  if (layer >= ((int64_t)1 << 32)) return KVD_ERR_UNSUPPORTED;
+  return KVD_OK;
+}
+
+kvd_status plan_decode(const PoolView& p, const kvd_decode_args* a, DecodePlan* out) {
+  if (!a) return KVD_ERR_INVALID_ARG;
+  if (a->b < 0 || a->n_q < 1 || a->max_blocks_per_seq < 1 || a->max_context_len < 0)
+    return KVD_ERR_INVALID_ARG;
+  if (a->n_q % p.n_kv != 0) return KVD_ERR_INVALID_ARG;
+  if (a->n_q / p.n_kv > 16) return KVD_ERR_UNSUPPORTED;
+  if (a->chunk_tokens < 0 || a->chunk_tokens % kvd::kBlock != 0) return KVD_ERR_INVALID_ARG;
+  if (a->score && (a->score_stride < 1 || a->score_stride < a->max_context_len))
+    return KVD_ERR_INVALID_ARG;
+  DecodePlan pl{};
+  const int64_t bound64 = std::min<int64_t>(a->max_context_len, (int64_t)kvd::kBlock * a->max_blocks_per_seq);
+  if (bound64 > (int64_t)1 << 30) return KVD_ERR_UNSUPPORTED;
+  pl.ctx_bound = (int32_t)bound64;
+  int64_t chunk = a->chunk_tokens;
+  if (chunk == 0) {
+    const int64_t total = (int64_t)std::max(a->b, 1) * p.n_kv * std::max(pl.ctx_bound, 1);
+    chunk = (total + kTargetWorkgroups - 1) / kTargetWorkgroups;
+    chunk = (chunk + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
+    chunk = std::max<int64_t>(chunk, kMinChunk);
+  }
+  const int64_t whole = std::max<int64_t>(kvd::kBlock, (pl.ctx_bound + 15) / 16 * 16);
+  if (chunk > whole) chunk = whole;
+  pl.chunk = (int32_t)chunk;
+  pl.n_chunks = (int32_t)std::max<int64_t>(1, (pl.ctx_bound + chunk - 1) / chunk);
+  if ((int64_t)pl.n_chunks * std::max(a->b, 1) * p.n_kv >= ((int64_t)1 << 31)) return KVD_ERR_UNSUPPORTED;
+  pl.final_direct = pl.n_chunks == 1;
+  pl.scores = a->score != nullptr;
+  pl.logit_stride = (pl.ctx_bound + 31) / 32 * 32 + 32;
+  size_t off = 0;
+  const size_t bq = (size_t)a->b * a->n_q;
+  if (!pl.final_direct) {
+    pl.off_part_o = off;
+    off = align256(off + bq * pl.n_chunks * p.head_dim * sizeof(float));
+    pl.off_part_lse = off;
+    off = align256(off + bq * pl.n_chunks * sizeof(float));
+  }
+  if (pl.scores) {
+    pl.off_logits = off;
+    off = align256(off + bq * pl.logit_stride * sizeof(float));
+    pl.off_lse2 = off;
+    off = align256(off + bq * sizeof(float));
+  }
+  pl.total = off;
+  *out = pl;
+  return KVD_OK;
+}
+
+kvd_status decode_common(const kvd_pool* pool, int32_t layer, const kvd_decode_args* a,
+                         void* stream, kvd_dtype want) {
+  if (!pool || !a) return KVD_ERR_INVALID_ARG;
+  const PoolView& p = pool->v;
+  if (p.dtype != want) return KVD_ERR_DTYPE;
+  if (layer < 0 || layer >= p.num_layers) return KVD_ERR_INVALID_ARG;
+  DecodePlan pl;
+  kvd_status st = plan_decode(p, a, &pl);
+  if (st != KVD_OK) return st;
+  if (a->b == 0) return KVD_OK;
+  if (!a->q || !a->block_table || !a->context_lens || !a->out) return KVD_ERR_INVALID_ARG;
+  if (pl.total > 0) {
+    if (!a->workspace || a->workspace_bytes < pl.total) return KVD_ERR_WORKSPACE;
+    if (((uintptr_t)a->workspace & 255) != 0) return KVD_ERR_WORKSPACE;
+  }
+  char* ws = static_cast<char*>(a->workspace);
+  kvd::DecodeLaunch L{};
+  L.layer_base = p.kv_base + (size_t)layer * (size_t)p.layer_bytes;
+  L.layer_bytes = (uint32_t)p.layer_bytes;
+  L.layer_scales = p.scale_base ? p.scale_base + (size_t)layer * p.num_blocks * p.n_kv * 2 : nullptr;
+  L.q = static_cast<const uint16_t*>(a->q);
+  L.block_table = a->block_table;
+  L.context_lens = a->context_lens;
+  L.b = a->b;
+  L.n_q = a->n_q;
+  L.n_kv = p.n_kv;
+  L.g = a->n_q / p.n_kv;
+  L.max_blocks = a->max_blocks_per_seq;
+  L.num_blocks = p.num_blocks;
+  L.ctx_bound = pl.ctx_bound;
+  L.chunk = pl.chunk;
+  L.n_chunks = pl.n_chunks;
+  L.out = static_cast<uint16_t*>(a->out);
+  L.lse_out = a->lse_out;
+  L.part_o = pl.final_direct ? nullptr : reinterpret_cast<float*>(ws + pl.off_part_o);
+  L.part_lse = pl.final_direct ? nullptr : reinterpret_cast<float*>(ws + pl.off_part_lse);
+  L.logits = pl.scores ? reinterpret_cast<float*>(ws + pl.off_logits) : nullptr;
+  L.lse2 = pl.scores ? reinterpret_cast<float*>(ws + pl.off_lse2) : nullptr;
+  L.logit_stride = pl.logit_stride;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kvd::launch_decode(L, p.head_dim, want == KVD_FP8_E4M3, pl.final_direct, pl.scores, s) != hipSuccess)
+    return KVD_ERR_HIP;
+  if (!pl.final_direct) {
+    if (kvd::launch_merge(L.part_o, L.part_lse, a->context_lens, pl.ctx_bound, pl.chunk, a->b,
+                          a->n_q, pl.n_chunks, p.head_dim, L.out, a->lse_out, L.lse2, s) != hipSuccess)
+      return KVD_ERR_HIP;
+  }
+  if (pl.scores) {
+    if (kvd::launch_score(L.logits, L.lse2, a->context_lens, pl.ctx_bound, a->b, a->n_q,
+                          pl.logit_stride, a->score, a->score_stride, a->score_weight, s) != hipSuccess)
+      return KVD_ERR_HIP;
+  }
+  return KVD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvd_status kvd_pool_bytes(const kvd_pool_desc* d, size_t* kv_bytes, size_t* scale_bytes) {
+  kvd_status st = check_desc(d);
+  if (st != KVD_OK) return st;
+  const size_t eb = d->dtype == KVD_BF16 ? 2 : 1;
+  const size_t tiles = (size_t)d->num_layers * d->num_blocks * d->n_kv;
+  if (kv_bytes) *kv_bytes = tiles * 2 * kvd::kBlock * d->head_dim * eb;
+  if (scale_bytes) *scale_bytes = d->dtype == KVD_FP8_E4M3 ? tiles * 2 * sizeof(float) : 0;
+  return KVD_OK;
+}
+
+kvd_status kvd_create_pool(const kvd_pool_desc* d, void* kv_base, float* scale_base, kvd_pool** out) {
+  if (!out) return KVD_ERR_INVALID_ARG;
+  kvd_status st = check_desc(d);
+  if (st != KVD_OK) return st;
+  if (!kv_base || ((uintptr_t)kv_base & 15) != 0) return KVD_ERR_INVALID_ARG;
+  if (d->dtype == KVD_FP8_E4M3) {
+    if (!scale_base || ((uintptr_t)scale_base & 3) != 0) return KVD_ERR_INVALID_ARG;
+  } else if (scale_base) {
+    return KVD_ERR_INVALID_ARG;
+  }
+  kvd_pool* p = new (std::nothrow) kvd_pool;
+  if (!p) return KVD_ERR_INVALID_ARG;
+  PoolView& v = p->v;
+  v.num_layers = d->num_layers;
+  v.num_blocks = d->num_blocks;
+  v.n_kv = d->n_kv;
+  v.head_dim = d->head_dim;
+  v.dtype = d->dtype;
+  v.kv_base = static_cast<char*>(kv_base);
+  v.scale_base = scale_base;
+  v.elem_bytes = d->dtype == KVD_BF16 ? 2 : 1;
+  v.tile_pair_bytes = 2LL * kvd::kBlock * d->head_dim * v.elem_bytes;
+  v.layer_bytes = (int64_t)d->num_blocks * d->n_kv * v.tile_pair_bytes;
+  *out = p;
+  return KVD_OK;
+}
+
+kvd_status kvd_destroy_pool(kvd_pool* pool) {
+  if (!pool) return KVD_ERR_INVALID_ARG;
+  delete pool;
+  return KVD_OK;
+}
+
+kvd_status kvd_write_kv(const kvd_pool* pool, int32_t layer, const void* k, const void* v,
+                        const int32_t* slot_mapping, int32_t n_tok, void* hip_stream) {
+  if (!pool) return KVD_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= pool->v.num_layers || n_tok < 0) return KVD_ERR_INVALID_ARG;
+  if (n_tok == 0) return KVD_OK;
+  if (!k || !v || !slot_mapping) return KVD_ERR_INVALID_ARG;
+  if ((int64_t)n_tok * pool->v.n_kv * pool->v.head_dim >= ((int64_t)1 << 40)) return KVD_ERR_UNSUPPORTED;
+  if (kvd::launch_write(pool->v, layer, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                        slot_mapping, n_tok, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+    return KVD_ERR_HIP;
+  return KVD_OK;
+}
+
+kvd_status kvd_decode_plan(const kvd_pool* pool, const kvd_decode_args* args, int32_t* chunk_tokens,
+                           int32_t* n_chunks) {
+  if (!pool) return KVD_ERR_INVALID_ARG;
+  DecodePlan pl;
+  kvd_status st = plan_decode(pool->v, args, &pl);
+  if (st != KVD_OK) return st;
+  if (chunk_tokens) *chunk_tokens = pl.chunk;
+  if (n_chunks) *n_chunks = pl.n_chunks;
+  return KVD_OK;
+}
+
+kvd_status kvd_decode_workspace_bytes(const kvd_pool* pool, const kvd_decode_args* args, size_t* bytes) {
+  if (!pool || !bytes) return KVD_ERR_INVALID_ARG;
+  DecodePlan pl;
+  kvd_status st = plan_decode(pool->v, args, &pl);
+  if (st != KVD_OK) return st;
+  *bytes = pl.total;
+  return KVD_OK;
+}
+
+kvd_status kvd_decode_attn(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args, void* hip_stream) {
+  return decode_common(pool, layer, args, hip_stream, KVD_BF16);
+}
+
+kvd_status kvd_decode_attn_fp8(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
+                               void* hip_stream) {
+  return decode_common(pool, layer, args, hip_stream, KVD_FP8_E4M3);
+}
+
+kvd_status kvd_merge_partials(const float* part_o, const float* part_lse, int32_t b, int32_t n_q,
+                              int32_t n_chunks, int32_t d_h, void* out_bf16, float* lse_out,
+                              void* hip_stream) {
+  if (b < 0 || n_q < 1 || n_chunks < 1) return KVD_ERR_INVALID_ARG;
+  if (d_h != 64 && d_h != 128) return KVD_ERR_UNSUPPORTED;
+  if (b == 0) return KVD_OK;
+  if (!part_o || !part_lse || !out_bf16) return KVD_ERR_INVALID_ARG;
+  if ((int64_t)b * n_q >= ((int64_t)1 << 31)) return KVD_ERR_UNSUPPORTED;
+  if (kvd::launch_merge(part_o, part_lse, nullptr, 0, 1, b, n_q, n_chunks, d_h,
+                        static_cast<uint16_t*>(out_bf16), lse_out, nullptr,
+                        static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+    return KVD_ERR_HIP;
+  return KVD_OK;
+}
+
+const char* kvd_status_string(kvd_status s) {
+  switch (s) {
+    case KVD_OK: return "KVD_OK";
+    case KVD_ERR_INVALID_ARG: return "KVD_ERR_INVALID_ARG";
+    case KVD_ERR_UNSUPPORTED: return "KVD_ERR_UNSUPPORTED";
+    case KVD_ERR_DTYPE: return "KVD_ERR_DTYPE";
+    case KVD_ERR_WORKSPACE: return "KVD_ERR_WORKSPACE";
+    case KVD_ERR_HIP: return "KVD_ERR_HIP";
+  }
+  return "KVD_ERR_UNKNOWN";
+}
+
+kvd_status kvd_debug_gather_offsets(const kvd_pool* pool, int32_t layer, const int32_t* block_table,
+                                    int32_t max_blocks_per_seq, int32_t b, int32_t n_tok,
+                                    int64_t* out_k, int64_t* out_v, void* hip_stream) {
+  if (!pool || layer < 0 || layer >= pool->v.num_layers) return KVD_ERR_INVALID_ARG;
+  if (b < 0 || n_tok < 0 || max_blocks_per_seq < 1) return KVD_ERR_INVALID_ARG;
+  if ((int64_t)n_tok > (int64_t)kvd::kBlock * max_blocks_per_seq) return KVD_ERR_INVALID_ARG;
+  if ((int64_t)b * n_tok == 0) return KVD_OK;
+  if (!block_table || !out_k || !out_v) return KVD_ERR_INVALID_ARG;
+  if (kvd::launch_debug_offsets(pool->v, layer, block_table, max_blocks_per_seq, b, n_tok, out_k, out_v,
+                                static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+    return KVD_ERR_HIP;
+  return KVD_OK;
+}
+
+kvd_status kvd_debug_fp8_decode(const uint8_t* codes, int32_t n, float* out, void* hip_stream) {
+  if (n < 0) return KVD_ERR_INVALID_ARG;
+  if (n == 0) return KVD_OK;
+  if (!codes || !out) return KVD_ERR_INVALID_ARG;
+  if (kvd::launch_debug_fp8_decode(codes, n, out, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+    return KVD_ERR_HIP;
+  return KVD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,347 @@
+// Split-context paged GQA decode attention for gfx950.
+//
+// One workgroup = one (sequence i, KV head j, context chunk c); its four waves
+// take the chunk's 16-token blocks two at a time ("pairs", 32 tokens) in
+// round-robin order.  For every pair a wave:
+//   * reads the two physical block ids from the block table and streams the
+//     pair's K and V tiles from HBM straight into registers, in the operand
+//     layout of the 16x16x32 bf16 MFMA (16-byte loads through a bounded buffer
+//     resource, so a bad block id reads zeros instead of faulting);
+//   * computes S = K q^T for all g query heads of KV head j at once (MFMA rows =
+//     tokens, columns = heads, so each K tile is read once and shared by the g
+//     heads -- the GQA saving);
+//   * folds S into a running max / sum per head (online softmax in the log2
+//     domain, fp32), and accumulates O^T += V^T P^T with a second MFMA whose
+//     rows are channels and columns heads.  P is split into bf16 hi + lo parts
+//     so that the product keeps ~16 bits of P (a single bf16 P would add a
+//     relative error of ~1e-3 to the output).
+// The four waves' (max, sum, O) are then combined through LDS and written
+// either as the final bf16 output (single chunk) or as an fp32 partial for
+// the log-sum-exp merge.
+//
+// Operand layout of v_mfma_f32_16x16x32_bf16 (lane l, G = l / 16, r = l % 16):
+// A[row r][k in group G], B[k in group G][col r], D[row 4G + q][col r], q < 4.
+// Which 8 of the 32 k indices a group holds is irrelevant here because A and
+// B use the same assignment; the code only relies on rows = r, cols = r and
+// the D layout.  Token/channel assignment chosen below:
+//   * S-tile t (t = 0, 1) row r  <-> pair token 8*(r/4) + 4t + r%4, so lane
+//     (G, r) ends up holding, for head r, the pair tokens 8G .. 8G+7
+//     (D row 4G+q of tile t is token 8G + 4t + q);
+//   * those 8 tokens are exactly the k group G of the P.V product, and they
+//     are 8 consecutive rows of block G/2 -- 16 contiguous bytes of one
+//     channel row of the channel-major V tile.
+#include "device_common.h"
+#include "kvd_internal.h"
+
+#include <math.h>
+
+namespace kvd {
+
+constexpr int kWaves = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int D, bool FP8>
+struct Pair {
+  static constexpr int E = FP8 ? 1 : 2;        // bytes per element
+  static constexpr int KU = D * E / 64;        // 16-byte K units per lane per S-tile
+  static constexpr int NM = D / 16;            // 16-channel tiles of the output
+  u32x4 k[2][KU];
+  u32x4 v[FP8 ? 1 : NM];                       // bf16 V: 16 B per lane per channel tile
+  u32x2 v8[FP8 ? NM : 1];                      // FP8 V: 8 B per lane per channel tile
+};
+
+// k index group G of MFMA step c covers these 8 channels of q and K.
+template <int D, bool FP8>
+__device__ inline int qk_channel0(int c, int G) {
+  return FP8 ? (64 * (c >> 1) + 16 * G + 8 * (c & 1)) : (32 * c + 8 * G);
+}
+
+template <int D, bool FP8, bool FINAL, bool SCORES>
+__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeLaunch a) {
+  using P = Pair<D, FP8>;
+  constexpr int E = P::E;
+  constexpr int NM = P::NM;
+  constexpr int NC = D / 32;                   // MFMA steps along the head dim
+  constexpr uint32_t TPB = 2u * kBlock * D * E;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+  const int G = lane >> 4;
+  const int r16 = lane & 15;
+
+  const int x = blockIdx.x;
+  const int j = x % a.n_kv;
+  const int i = (x / a.n_kv) % a.b;
+  const int c = x / (a.n_kv * a.b);
+
+  int s = a.context_lens[i];
+  s = s < 0 ? 0 : (s > a.ctx_bound ? a.ctx_bound : s);
+  const int lo = c * a.chunk;
+  const int ntok = min(s, lo + a.chunk) - lo;
+  if (!FINAL && ntok <= 0) return;             // empty chunk: the merge skips it
+
+  const int g = a.g;
+  const bool head_ok = r16 < g;
+
+  // q as the B operand of S = K q^T: column r16 = query head j*g + r16.
+  bf16x8 qf[NC];
+  {
+    const uint16_t* qrow = a.q + ((size_t)i * a.n_q + (size_t)j * g + r16) * D;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (head_ok) raw = *reinterpret_cast<const u32x4*>(qrow + qk_channel0<D, FP8>(cc, G));
+      qf[cc] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.layer_base, a.layer_bytes);
+  const int32_t* bt = a.block_table + (size_t)i * a.max_blocks + lo / kBlock;
+  const float qk_scale = kLog2e * (1.0f / sqrtf((float)D));
+
+  float m = -INFINITY;                          // running max of head r16 (log2 domain)
+  float l = 0.f;                                // this lane's share of the running sum
+  f32x4 o[NM];
+#pragma unroll
+  for (int mm = 0; mm < NM; ++mm) o[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int npairs = (ntok + 31) >> 5;
+  for (int p = wave; p < npairs; p += kWaves) {
+    const int tok0 = p << 5;
+    const int nvalid = min(32, ntok - tok0);
+    const int32_t pid0 = bt[2 * p];
+    const int32_t pid1 = nvalid > kBlock ? bt[2 * p + 1] : -1;
+    const uint32_t t0 = tile_pair_offset(pid0, j, a.num_blocks, a.n_kv, TPB);
+    const uint32_t t1 = tile_pair_offset(pid1, j, a.num_blocks, a.n_kv, TPB);
+
+    P d;
+    {
+      // K: S-tile t, row r16 -> block r16/8, in-block row 8*((r16/4)&1) + 4t + r16%4;
+      // this lane's 16-byte units sit at byte 64u + 16G of that row.
+      const uint32_t tk = r16 < 8 ? t0 : t1;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = 8 * ((r16 >> 2) & 1) + 4 * t + (r16 & 3);
+#pragma unroll
+        for (int u = 0; u < P::KU; ++u) {
+          const uint32_t off = tk + (uint32_t)(row * D * E + 64 * u + 16 * G);
+          d.k[t][u] = load16(rs, tk == kOutOfRange ? kOutOfRange : off);
+        }
+      }
+      // V (channel-major): channel tile mm, channel 16mm + r16, rows 8(G&1) .. +7
+      // of block G/2.
+      const uint32_t tv = G < 2 ? t0 : t1;
+#pragma unroll
+      for (int mm = 0; mm < NM; ++mm) {
+        const uint32_t off = tv + (uint32_t)((v_elem(8 * (G & 1), 16 * mm + r16, D)) * E);
+        const uint32_t o2 = tv == kOutOfRange ? kOutOfRange : off;
+        if constexpr (FP8) d.v8[mm] = load8(rs, o2);
+        else d.v[mm] = load16(rs, o2);
+      }
+    }
+
+    float sK = 1.f, sV = 1.f;
+    if constexpr (FP8) {
+      // fp32 scales of this lane's block (G/2) for K and V; zero for a bad id.
+      const float* sc = a.layer_scales;
+      const float sk0 = t0 == kOutOfRange ? 0.f : sc[((size_t)pid0 * a.n_kv + j) * 2 + 0];
+      const float sv0 = t0 == kOutOfRange ? 0.f : sc[((size_t)pid0 * a.n_kv + j) * 2 + 1];
+      const float sk1 = t1 == kOutOfRange ? 0.f : sc[((size_t)pid1 * a.n_kv + j) * 2 + 0];
+      const float sv1 = t1 == kOutOfRange ? 0.f : sc[((size_t)pid1 * a.n_kv + j) * 2 + 1];
+      sK = G < 2 ? sk0 : sk1;
+      sV = G < 2 ? sv0 : sv1;
+    }
+
+    // S = K q^T for both S-tiles.
+    f32x4 sacc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        bf16x8 kf;
+        if constexpr (FP8) {
+          const u32x4 w = d.k[t][cc >> 1];
+          kf = (cc & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
+        } else {
+          kf = __builtin_bit_cast(bf16x8, d.k[t][cc]);
+        }
+        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[cc], sacc[t], 0, 0, 0);
+      }
+    }
+
+    // Scaled scores; lane element e = 4t + q is pair token 8G + e.
+    float xs[8];
+    const float sc_all = qk_scale * sK;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xs[4 * t + q] = sacc[t][q] * sc_all;
+
+    const int my_valid = min(8, max(0, nvalid - 8 * G));   // valid tokens among my 8
+    if (nvalid < 32) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e >= my_valid) xs[e] = -INFINITY;
+    }
+
+    if constexpr (SCORES) {
+      if (head_ok) {
+        float* dst = a.logits + ((size_t)i * a.n_q + (size_t)j * g + r16) * a.logit_stride +
+                     lo + tok0 + 8 * G;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{xs[0], xs[1], xs[2], xs[3]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{xs[4], xs[5], xs[6], xs[7]};
+      }
+    }
+
+    float mx = xs[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, xs[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float corr = __builtin_amdgcn_exp2f(m - m_use);
+    m = m_new;
+
+    float pv[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pv[e] = __builtin_amdgcn_exp2f(xs[e] - m_use);
+      psum += pv[e];
+    }
+    l = l * corr + psum;
+#pragma unroll
+    for (int mm = 0; mm < NM; ++mm) o[mm] *= corr;
+
+    bf16x8 phi, plo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = pv[e] * sV;
+      const __bf16 h = (__bf16)pe;
+      phi[e] = h;
+      plo[e] = (__bf16)(pe - (float)h);
+    }
+
+    // Zero V of tokens past the end so that stale (even NaN) rows contribute 0.
+    if (nvalid < 32) {
+      if constexpr (FP8) {
+        uint32_t keep[2];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          uint32_t mk = 0;
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb)
+            if (4 * w + bb < my_valid) mk |= 0xFFu << (8 * bb);
+          keep[w] = mk;
+        }
+#pragma unroll
+        for (int mm = 0; mm < NM; ++mm) {
+          d.v8[mm][0] &= keep[0];
+          d.v8[mm][1] &= keep[1];
+        }
+      } else {
+        uint32_t keep[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          keep[w] = (2 * w < my_valid ? 0x0000FFFFu : 0u) | (2 * w + 1 < my_valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int mm = 0; mm < NM; ++mm)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) d.v[mm][w] &= keep[w];
+      }
+    }
+
+    // O^T[channel][head] += V^T P^T, rows = channels 16mm + 4G + q, cols = heads.
+#pragma unroll
+    for (int mm = 0; mm < NM; ++mm) {
+      bf16x8 vf;
+      if constexpr (FP8) vf = e4m3x8_to_bf16x8(d.v8[mm][0], d.v8[mm][1]);
+      else vf = __builtin_bit_cast(bf16x8, d.v[mm]);
+      o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi, o[mm], 0, 0, 0);
+      o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo, o[mm], 0, 0, 0);
+    }
+  }
+
+  // Whole-head sum of this wave.
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+
+  // Combine the waves: common max, rescaled sums and outputs.
+  __shared__ float sh_m[kWaves][16];
+  __shared__ float sh_l[kWaves][16];
+  __shared__ f32x4 sh_o[kWaves][NM][64];
+  if (G == 0) {
+    sh_m[wave][r16] = m;
+    sh_l[wave][r16] = l;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh_m[w][r16]);
+  float L = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) L += sh_l[w][r16] * __builtin_amdgcn_exp2f(sh_m[w][r16] - M);
+  }
+  const float f_own = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+#pragma unroll
+  for (int mm = 0; mm < NM; ++mm) sh_o[wave][mm][lane] = o[mm] * f_own;
+  __syncthreads();
+
+  const bool empty = !(L > 0.f);
+  const float inv_l = empty ? 0.f : 1.0f / L;
+  const float lse2 = empty ? -INFINITY : M + __log2f(L);
+  const size_t ih = (size_t)i * a.n_q + (size_t)j * g + r16;   // valid when head_ok
+  for (int mm = wave; mm < NM; mm += kWaves) {
+    f32x4 acc = sh_o[0][mm][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) acc += sh_o[w][mm][lane];
+    acc *= inv_l;
+    if (!head_ok) continue;
+    const int ch = 16 * mm + 4 * G;
+    if constexpr (FINAL) {
+      uint32_t lo2 = (uint32_t)float_to_bf16_bits(acc[0]) | ((uint32_t)float_to_bf16_bits(acc[1]) << 16);
+      uint32_t hi2 = (uint32_t)float_to_bf16_bits(acc[2]) | ((uint32_t)float_to_bf16_bits(acc[3]) << 16);
+      *reinterpret_cast<u32x2*>(a.out + ih * D + ch) = u32x2{lo2, hi2};
+    } else {
+      *reinterpret_cast<f32x4*>(a.part_o + (ih * a.n_chunks + c) * D + ch) = acc;
+    }
+  }
+  if (wave == 0 && G == 0 && head_ok) {
+    if constexpr (FINAL) {
+      if (a.lse_out) a.lse_out[ih] = lse2 * kLn2;
+      if constexpr (SCORES) a.lse2[ih] = lse2;
+    } else {
+      a.part_lse[ih * a.n_chunks + c] = lse2 * kLn2;
+    }
+  }
+}
+
+template <int D, bool FP8>
+static hipError_t launch_d(const DecodeLaunch& a, bool final_direct, bool scores,
+                           hipStream_t stream) {
+  const dim3 grid((unsigned)((size_t)a.n_chunks * a.b * a.n_kv));
+  const dim3 block(64 * kWaves);
+  if (final_direct) {
+    if (scores) hipLaunchKernelGGL((decode_kernel<D, FP8, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_kernel<D, FP8, true, false>), grid, block, 0, stream, a);
+  } else {
+    if (scores) hipLaunchKernelGGL((decode_kernel<D, FP8, false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_kernel<D, FP8, false, false>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeLaunch& a, int head_dim, bool fp8, bool final_direct,
+                         bool scores, hipStream_t stream) {
+  if (head_dim == 128)
+    return fp8 ? launch_d<128, true>(a, final_direct, scores, stream)
+               : launch_d<128, false>(a, final_direct, scores, stream);
+  return fp8 ? launch_d<64, true>(a, final_direct, scores, stream)
+             : launch_d<64, false>(a, final_direct, scores, stream);
+}
+
+}  // namespace kvd

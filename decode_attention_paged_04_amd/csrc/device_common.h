@@ -1,0 +1,76 @@
+// Device helpers shared by the kernels: vector types, bounded buffer loads,
+// the pool addressing rule and the E4M3 -> bf16 widening.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvd {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// Buffer resource word 3 for gfx9-family raw buffers (32-bit data format);
+// with stride 0 the record count is a byte count and every load outside
+// [0, num_records) returns zeros instead of touching memory.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0xFFFFFFFFu;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRawBufferWord3);
+}
+
+__device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ inline u32x2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// Byte offset, from the start of a layer, of the tile pair of (block p, KV head
+// j); kOutOfRange for a block id outside the pool, so every load through it
+// reads zeros.
+__host__ __device__ inline uint32_t tile_pair_offset(int32_t p, int32_t j, int32_t num_blocks,
+                                                     int32_t n_kv, uint32_t tile_pair_bytes) {
+  if ((uint32_t)p >= (uint32_t)num_blocks) return kOutOfRange;
+  return ((uint32_t)p * (uint32_t)n_kv + (uint32_t)j) * tile_pair_bytes;
+}
+
+// Element offsets inside a tile pair: K token-major, V channel-major.
+__host__ __device__ inline uint32_t k_elem(int row, int ch, int head_dim) {
+  return (uint32_t)(row * head_dim + ch);
+}
+__host__ __device__ inline uint32_t v_elem(int row, int ch, int head_dim) {
+  return (uint32_t)(16 * head_dim + ch * 16 + row);
+}
+
+// Widen 8 E4M3FN codes (two dwords, code k in byte k % 4 of dword k / 4) to
+// bf16 in order.  E4M3FN -> bf16 is exact: 3 mantissa bits fit in 7 and the
+// exponent range (2^-9 .. 448) lies inside bf16's normal range.  gfx950's
+// scaled conversion is used with scale 1.0, i.e. a plain conversion.
+__device__ inline bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+__device__ inline float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Round to nearest even; NaN stays NaN.
+__device__ inline uint16_t float_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+}  // namespace kvd

@@ -1,0 +1,102 @@
+// Log-sum-exp merge of per-chunk partials, and the fused cumulative-score
+// update that needs the merged lse.
+#include "device_common.h"
+#include "kvd_internal.h"
+
+#include <math.h>
+
+namespace kvd {
+
+constexpr float kLog2eM = 1.4426950408889634f;
+
+// One workgroup per (sequence, query head); thread t owns channel t.
+// lse = M + ln(sum_c exp(lse_c - M)), out = sum_c exp(lse_c - lse) * o_c.
+template <int D>
+__global__ __launch_bounds__(D) void merge_kernel(const float* __restrict__ part_o,
+                                                  const float* __restrict__ part_lse,
+                                                  const int32_t* __restrict__ context_lens,
+                                                  int32_t ctx_bound, int32_t chunk, int32_t n_q,
+                                                  int32_t n_chunks, uint16_t* __restrict__ out,
+                                                  float* __restrict__ lse_out,
+                                                  float* __restrict__ lse2) {
+  const size_t ih = blockIdx.x;
+  const int i = (int)(ih / n_q);
+  int nc = n_chunks;
+  if (context_lens) {
+    int s = context_lens[i];
+    s = s < 0 ? 0 : (s > ctx_bound ? ctx_bound : s);
+    nc = min(n_chunks, (s + chunk - 1) / chunk);
+  }
+  const float* pl = part_lse + ih * n_chunks;
+  float M = -INFINITY;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, pl[c]);
+  const int t = threadIdx.x;
+  if (M == -INFINITY) {
+    out[ih * D + t] = 0;
+    if (t == 0) {
+      if (lse_out) lse_out[ih] = -INFINITY;
+      if (lse2) lse2[ih] = -INFINITY;
+    }
+    return;
+  }
+  float L = 0.f;
+  for (int c = 0; c < nc; ++c) L += expf(pl[c] - M);
+  const float lse = M + logf(L);
+  const float* po = part_o + ih * n_chunks * D + t;
+  float acc = 0.f;
+  for (int c = 0; c < nc; ++c) {
+    const float w = expf(pl[c] - lse);
+    if (w != 0.f) acc += w * po[(size_t)c * D];
+  }
+  out[ih * D + t] = float_to_bf16_bits(acc);
+  if (t == 0) {
+    if (lse_out) lse_out[ih] = lse;
+    if (lse2) lse2[ih] = lse * kLog2eM;
+  }
+}
+
+// score[i][t] += weight / n_q * sum_h exp2(x[i][h][t] - lse2[i][h]) for t < s_i,
+// x being the log2-domain scaled scores the decode kernel stored.
+__global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ logits,
+                                                    const float* __restrict__ lse2,
+                                                    const int32_t* __restrict__ context_lens,
+                                                    int32_t ctx_bound, int32_t n_q,
+                                                    int32_t stride, float* __restrict__ score,
+                                                    int32_t score_stride, float w_over_nq) {
+  const int i = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  int s = context_lens[i];
+  s = s < 0 ? 0 : (s > ctx_bound ? ctx_bound : s);
+  if (t >= s) return;
+  const float* x = logits + (size_t)i * n_q * stride + t;
+  const float* ls = lse2 + (size_t)i * n_q;
+  float acc = 0.f;
+  for (int h = 0; h < n_q; ++h) acc += __builtin_amdgcn_exp2f(x[(size_t)h * stride] - ls[h]);
+  score[(size_t)i * score_stride + t] += w_over_nq * acc;
+}
+
+hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_t* context_lens,
+                        int32_t ctx_bound, int32_t chunk, int32_t b, int32_t n_q,
+                        int32_t n_chunks, int32_t head_dim, uint16_t* out, float* lse_out,
+                        float* lse2, hipStream_t stream) {
+  const dim3 grid((unsigned)((size_t)b * n_q));
+  if (head_dim == 128)
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(128), 0, stream, part_o, part_lse,
+                       context_lens, ctx_bound, chunk, n_q, n_chunks, out, lse_out, lse2);
+  else
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, stream, part_o, part_lse,
+                       context_lens, ctx_bound, chunk, n_q, n_chunks, out, lse_out, lse2);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const float* logits, const float* lse2, const int32_t* context_lens,
+                        int32_t ctx_bound, int32_t b, int32_t n_q, int32_t logit_stride,
+                        float* score, int32_t score_stride, float weight, hipStream_t stream) {
+  if (ctx_bound <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((ctx_bound + 255) / 256), (unsigned)b);
+  hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, stream, logits, lse2, context_lens,
+                     ctx_bound, n_q, logit_stride, score, score_stride, weight / (float)n_q);
+  return hipGetLastError();
+}
+
+}  // namespace kvd

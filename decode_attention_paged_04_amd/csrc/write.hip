@@ -1,0 +1,182 @@
+// Storing new tokens into the pool (bf16 copy, FP8 E4M3 quantisation) and the
+// test hooks that expose the decode kernels' addressing and FP8 widening.
+#include "device_common.h"
+#include "kvd_internal.h"
+
+#include <math.h>
+
+namespace kvd {
+
+// One thread per (token, KV head, channel): K goes token-major, V channel-major.
+template <int D>
+__global__ __launch_bounds__(256) void write_bf16_kernel(char* __restrict__ layer_base,
+                                                         int32_t num_blocks, int32_t n_kv,
+                                                         const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v,
+                                                         const int32_t* __restrict__ slots,
+                                                         int32_t n_tok) {
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t total = (size_t)n_tok * n_kv * D;
+  if (e >= total) return;
+  const int ch = (int)(e % D);
+  const int j = (int)((e / D) % n_kv);
+  const size_t t = e / ((size_t)D * n_kv);
+  const int32_t slot = slots[t];
+  if (slot < 0) return;
+  const int32_t p = slot / kBlock;
+  const int row = slot % kBlock;
+  if (p >= num_blocks) return;
+  uint16_t* tile = reinterpret_cast<uint16_t*>(layer_base + ((size_t)p * n_kv + j) * (2 * kBlock * D * 2));
+  tile[k_elem(row, ch, D)] = k[e];
+  tile[v_elem(row, ch, D)] = v[e];
+}
+
+// Nearest-even E4M3FN code of y, saturating at +-448 (sign kept, -0 -> 0x80).
+__device__ inline uint32_t e4m3_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  uint32_t code;
+  if (!(a < 448.0f)) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {                       // below 2^-6: grid of m * 2^-9
+    code = (uint32_t)rintf(a * 512.0f);             // exact scaling; rint ties to even
+  } else {
+    const uint32_t ab = __float_as_uint(a);
+    const uint32_t e = (ab >> 23) - 127u + 7u;      // biased E4M3 exponent, 1..15
+    const uint32_t mant = ab & 0x7FFFFFu;
+    uint32_t q = (e << 3) | (mant >> 20);
+    const uint32_t rem = mant & 0xFFFFFu;
+    q += (rem > 0x80000u) || (rem == 0x80000u && (q & 1u));   // carry may bump the exponent
+    code = q;
+  }
+  return sign | code;
+}
+
+// One wave per (run of consecutive slots starting at a block's row 0, KV head,
+// K|V): absmax over the run, scale = absmax / 448, codes of x / scale.
+template <int D>
+__global__ __launch_bounds__(64) void write_fp8_kernel(char* __restrict__ layer_base,
+                                                       float* __restrict__ layer_scales,
+                                                       int32_t num_blocks, int32_t n_kv,
+                                                       const uint16_t* __restrict__ k,
+                                                       const uint16_t* __restrict__ v,
+                                                       const int32_t* __restrict__ slots,
+                                                       int32_t n_tok) {
+  const int t = blockIdx.x;
+  const int j = blockIdx.y;
+  const int which = blockIdx.z;                     // 0: K, 1: V
+  const int lane = threadIdx.x;
+  const int32_t slot = slots[t];
+  if (slot < 0 || (slot % kBlock) != 0) return;
+  const int32_t p = slot / kBlock;
+  if (p >= num_blocks) return;
+  int n = 1;
+  while (n < kBlock && t + n < n_tok && slots[t + n] == slot + n) ++n;
+
+  const uint16_t* src = (which ? v : k) + ((size_t)t * n_kv + j) * D;
+  const size_t row_stride = (size_t)n_kv * D;
+  float am = 0.f;
+  for (int r = 0; r < n; ++r)
+    for (int ch = lane; ch < D; ch += 64) am = fmaxf(am, fabsf(bf16_bits_to_float(src[r * row_stride + ch])));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  const float scale = am / 448.0f;
+
+  uint8_t* tile = reinterpret_cast<uint8_t*>(layer_base + ((size_t)p * n_kv + j) * (2 * kBlock * D));
+  for (int r = 0; r < n; ++r) {
+    for (int ch = lane; ch < D; ch += 64) {
+      const float x = bf16_bits_to_float(src[r * row_stride + ch]);
+      const uint32_t code = scale == 0.f ? 0u : e4m3_encode(x / scale);
+      tile[which ? v_elem(r, ch, D) : k_elem(r, ch, D)] = (uint8_t)code;
+    }
+  }
+  if (lane == 0) layer_scales[((size_t)p * n_kv + j) * 2 + which] = scale;
+}
+
+hipError_t launch_write(const PoolView& pv, int32_t layer, const uint16_t* k, const uint16_t* v,
+                        const int32_t* slots, int32_t n_tok, hipStream_t stream) {
+  char* base = pv.kv_base + (size_t)layer * (size_t)pv.layer_bytes;
+  const int D = pv.head_dim;
+  if (pv.dtype == KVD_BF16) {
+    const size_t total = (size_t)n_tok * pv.n_kv * D;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (D == 128)
+      hipLaunchKernelGGL(write_bf16_kernel<128>, grid, dim3(256), 0, stream, base, pv.num_blocks,
+                         pv.n_kv, k, v, slots, n_tok);
+    else
+      hipLaunchKernelGGL(write_bf16_kernel<64>, grid, dim3(256), 0, stream, base, pv.num_blocks,
+                         pv.n_kv, k, v, slots, n_tok);
+  } else {
+    float* sc = pv.scale_base + (size_t)layer * pv.num_blocks * pv.n_kv * 2;
+    const dim3 grid((unsigned)n_tok, (unsigned)pv.n_kv, 2);
+    if (D == 128)
+      hipLaunchKernelGGL(write_fp8_kernel<128>, grid, dim3(64), 0, stream, base, sc,
+                         pv.num_blocks, pv.n_kv, k, v, slots, n_tok);
+    else
+      hipLaunchKernelGGL(write_fp8_kernel<64>, grid, dim3(64), 0, stream, base, sc,
+                         pv.num_blocks, pv.n_kv, k, v, slots, n_tok);
+  }
+  return hipGetLastError();
+}
+
+// Element offsets of K[t][0] and V[t][0] through the decode kernels' rule.
+__global__ __launch_bounds__(256) void debug_offsets_kernel(int64_t layer_elem0, int32_t num_blocks,
+                                                            int32_t n_kv, int32_t head_dim,
+                                                            int32_t elem_bytes,
+                                                            const int32_t* __restrict__ bt,
+                                                            int32_t max_blocks, int32_t b,
+                                                            int32_t n_tok, int64_t* out_k,
+                                                            int64_t* out_v) {
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t total = (size_t)b * n_kv * n_tok;
+  if (e >= total) return;
+  const int t = (int)(e % n_tok);
+  const int j = (int)((e / n_tok) % n_kv);
+  const int i = (int)(e / ((size_t)n_tok * n_kv));
+  const int32_t p = bt[(size_t)i * max_blocks + t / kBlock];
+  const uint32_t tpb = (uint32_t)(2 * kBlock * head_dim * elem_bytes);
+  const uint32_t off = tile_pair_offset(p, j, num_blocks, n_kv, tpb);
+  if (off == kOutOfRange) {
+    out_k[e] = -1;
+    out_v[e] = -1;
+    return;
+  }
+  const int64_t tile_elem = layer_elem0 + (int64_t)(off / (uint32_t)elem_bytes);
+  out_k[e] = tile_elem + k_elem(t % kBlock, 0, head_dim);
+  out_v[e] = tile_elem + v_elem(t % kBlock, 0, head_dim);
+}
+
+hipError_t launch_debug_offsets(const PoolView& pv, int32_t layer, const int32_t* bt,
+                                int32_t max_blocks, int32_t b, int32_t n_tok, int64_t* out_k,
+                                int64_t* out_v, hipStream_t stream) {
+  const size_t total = (size_t)b * pv.n_kv * n_tok;
+  if (total == 0) return hipSuccess;
+  const int64_t layer_elem0 = (int64_t)layer * pv.layer_bytes / pv.elem_bytes;
+  hipLaunchKernelGGL(debug_offsets_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, layer_elem0, pv.num_blocks, pv.n_kv, pv.head_dim,
+                     (int32_t)pv.elem_bytes, bt, max_blocks, b, n_tok, out_k, out_v);
+  return hipGetLastError();
+}
+
+// Each thread widens 8 codes with the decode kernels' routine.
+__global__ __launch_bounds__(256) void debug_fp8_kernel(const uint8_t* __restrict__ codes,
+                                                        int32_t n, float* __restrict__ out) {
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  const int base = q * 8;
+  if (base >= n) return;
+  uint32_t w[2] = {0u, 0u};
+  for (int e = 0; e < 8 && base + e < n; ++e) w[e >> 2] |= (uint32_t)codes[base + e] << (8 * (e & 3));
+  const bf16x8 r = e4m3x8_to_bf16x8(w[0], w[1]);
+  for (int e = 0; e < 8 && base + e < n; ++e) out[base + e] = (float)r[e];
+}
+
+hipError_t launch_debug_fp8_decode(const uint8_t* codes, int32_t n, float* out,
+                                   hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int groups = (n + 7) / 8;
+  hipLaunchKernelGGL(debug_fp8_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
+                     stream, codes, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace kvd

@@ -1,0 +1,206 @@
+/*
+ * libkvdecode -- one decode step of grouped-query attention over a paged KV
+ * cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For every sequence i of a batch and every query head h,
+ * the single new query q[i][h] attends to all s_i cached K/V rows of its
+ * sequence: scores q.k / sqrt(d_h), a softmax over them, and the weighted sum
+ * of the V rows (froggydisk "LLM에서 KV 캐시는 얼마나 생길까", section
+ * "KV 캐시란").  Query heads share KV heads in contiguous groups of
+ * g = n_q / n_kv: query head h reads KV head floor(h / g) (same section: 32
+ * query heads over 8 KV heads).  s_i counts every cached token including the
+ * current one; there is no mask.  The rows are found through a per-sequence
+ * block table over fixed 16-token blocks, so the physical placement of the
+ * blocks cannot change the result (same page, PagedAttention paragraph).
+ *
+ * Ownership.  Every device buffer is allocated, owned and freed by the
+ * caller.  The library never allocates or frees device memory and keeps no
+ * mutable global state.  A pool handle holds host metadata only; it is
+ * immutable after creation and may be shared by threads and streams.
+ * Buffers must stay alive until the stream work that uses them completes.
+ *
+ * Errors.  Every call returns a kvd_status and nothing aborts.  Shape,
+ * dtype and size errors are detected on the host before any launch; launch
+ * failures map to KVD_ERR_HIP.  No call synchronises the device.  Values that
+ * live in device memory (context lengths, block ids, slot ids) are not
+ * validated on the host: context lengths are clamped into [0, bound] (see
+ * kvd_decode_args), block ids outside [0, num_blocks) read as zero K/V, and
+ * write slots outside the pool are skipped.  No device access can leave the
+ * caller's buffers.
+ *
+ * Streams.  `hip_stream` is a hipStream_t passed as void*; NULL is the null
+ * stream.  All work of one call is enqueued on that stream in order.
+ */
+#ifndef KVDECODE_H
+#define KVDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVD_OK = 0,
+  KVD_ERR_INVALID_ARG = 1,  /* null pointer, negative or inconsistent size   */
+  KVD_ERR_UNSUPPORTED = 2,  /* valid but not built: d_h, block size, sizes   */
+  KVD_ERR_DTYPE = 3,        /* bf16 entry point on an FP8 pool or vice versa */
+  KVD_ERR_WORKSPACE = 4,    /* workspace missing or too small                */
+  KVD_ERR_HIP = 5           /* a HIP launch or query failed                  */
+} kvd_status;
+
+/* KV element type of a pool.
+ * KVD_FP8_E4M3 is the OCP E4M3FN format (1 sign, 4 exponent, 3 mantissa bits,
+ * bias 7, largest finite 448, codes 0x7F/0xFF NaN, no infinities), the format
+ * with the 448 maximum in froggydisk's FP8 table. */
+typedef enum { KVD_BF16 = 0, KVD_FP8_E4M3 = 1 } kvd_dtype;
+
+/* Shape of a paged KV pool.  block_size must be 16 (the block size of the
+ * PagedAttention paragraph); head_dim must be 64 or 128. */
+typedef struct {
+  int32_t num_layers;
+  int32_t num_blocks;   /* physical blocks; block ids are shared by all layers */
+  int32_t block_size;   /* = 16                                                */
+  int32_t n_kv;         /* KV heads                                            */
+  int32_t head_dim;     /* 64 or 128                                           */
+  kvd_dtype dtype;
+} kvd_pool_desc;
+
+/* Pool layout in device memory (w = 2 bytes for bf16, 1 for FP8).
+ *
+ *   tile pair of (layer l, physical block p, KV head j) starts at element
+ *       T = ((l * num_blocks + p) * n_kv + j) * (2 * 16 * head_dim)
+ *   K of in-block row t (0..15), channel c:  T + t * head_dim + c
+ *   V of in-block row t,         channel c:  T + 16 * head_dim + c * 16 + t
+ *
+ * so one (block, head) is one contiguous 2*16*head_dim*w-byte region: the K
+ * tile token-major, then the V tile channel-major.  Logical token t of a
+ * sequence lives in physical block table[t / 16] at in-block row t % 16.
+ * FP8 pools add fp32 scales, one per (layer, block, KV head) for K and one
+ * for V, at scale_base[((l * num_blocks + p) * n_kv + j) * 2 + {0: K, 1: V}];
+ * a stored element decodes to code_value * scale.
+ * Each layer of the pool must be smaller than 4 GiB. */
+typedef struct kvd_pool kvd_pool;
+
+/* Bytes the caller must allocate for a pool: kv_bytes for K/V (256-byte
+ * alignment recommended) and scale_bytes for FP8 scales (0 for bf16).
+ * Either output pointer may be NULL. */
+kvd_status kvd_pool_bytes(const kvd_pool_desc* desc, size_t* kv_bytes, size_t* scale_bytes);
+
+/* Create a host handle over caller-owned device memory laid out as above.
+ * kv_base: device pointer to kv_bytes bytes, 16-byte aligned.
+ * scale_base: device pointer to scale_bytes bytes (FP8), NULL for bf16.
+ * Host only: makes no HIP call.  *out is set only on KVD_OK. */
+kvd_status kvd_create_pool(const kvd_pool_desc* desc, void* kv_base, float* scale_base,
+                           kvd_pool** out);
+kvd_status kvd_destroy_pool(kvd_pool* pool);
+
+/* Store n_tok new tokens' K and V of one layer into the pool.
+ * k, v: device bf16 [n_tok][n_kv][head_dim], contiguous.
+ * slot_mapping: device int32 [n_tok]; token r goes to physical block
+ *   slot / 16, in-block row slot % 16.  Negative slots are skipped (padding),
+ *   as are slots past the pool.
+ * bf16 pools: a plain copy into the layout.
+ * FP8 pools: every (block, KV head) gets one scale for K and one for V,
+ *   scale = absmax / 448 over the block's rows written by this call (fp32,
+ *   IEEE division), and each element is stored as the nearest-even E4M3 code
+ *   of x / scale (fp32 division), saturated to +-448; an all-zero tile gets
+ *   scale 0 and zero codes.  (Scale per block and head, not per layer as the
+ *   FP8 paragraph of froggydisk's page suggests.)  A block must be written
+ *   from row 0 by consecutive entries of one call (slot, slot+1, ...), the
+ *   way a prompt is stored; entries that continue a block written by an
+ *   earlier call are skipped (appending with re-quantisation is not built).
+ *   Rows of a block past the last one written keep whatever they held and are
+ *   never read as long as the context lengths exclude them. */
+kvd_status kvd_write_kv(const kvd_pool* pool, int32_t layer, const void* k, const void* v,
+                        const int32_t* slot_mapping, int32_t n_tok, void* hip_stream);
+
+/* Arguments of one decode-attention call on one layer. */
+typedef struct {
+  int32_t b;                  /* sequences                                            */
+  int32_t n_q;                /* query heads, a multiple of the pool's n_kv           */
+  int32_t max_blocks_per_seq; /* row length of block_table                            */
+  int32_t max_context_len;    /* host-known bound on every s_i (sizes the launch)     */
+  const void* q;              /* device bf16 [b][n_q][head_dim], post-RoPE            */
+  const int32_t* block_table; /* device int32 [b][max_blocks_per_seq]; entries at or  */
+                              /* past ceil(s_i / 16) are never read                   */
+  const int32_t* context_lens;/* device int32 [b]; s_i is clamped into               */
+                              /* [0, min(max_context_len, 16 * max_blocks_per_seq)]  */
+  void* out;                  /* device bf16 [b][n_q][head_dim]; s_i = 0 gives zeros  */
+  float* lse_out;             /* optional device fp32 [b][n_q]: natural-log           */
+                              /* log-sum-exp of the scaled scores (-inf if s_i = 0)   */
+  int32_t chunk_tokens;       /* context split: 0 = automatic, else a multiple of 16  */
+  void* workspace;            /* device scratch of kvd_decode_workspace_bytes bytes,  */
+  size_t workspace_bytes;     /* 256-byte aligned; may be NULL when that size is 0    */
+  float* score;               /* optional device fp32 [b][score_stride] cumulative    */
+  int32_t score_stride;       /* score; >= max_context_len when score is set          */
+  float score_weight;         /* score[i][t] += score_weight * mean_h alpha_h(t)      */
+} kvd_decode_args;
+
+/* How a decode call splits the context: chunk length in tokens and number of
+ * chunks.  Pure host function of the pool and the arguments. */
+kvd_status kvd_decode_plan(const kvd_pool* pool, const kvd_decode_args* args,
+                           int32_t* chunk_tokens, int32_t* n_chunks);
+
+/* Workspace bytes a decode call with these arguments needs (0 when the whole
+ * context fits one chunk and no score is requested).  Pure host function. */
+kvd_status kvd_decode_workspace_bytes(const kvd_pool* pool, const kvd_decode_args* args,
+                                      size_t* bytes);
+
+/* One decode-attention step of one layer on a bf16 pool.
+ * Each (sequence, KV head, context chunk) is processed by one workgroup that
+ * streams the chunk's K/V blocks once and serves all g query heads of the KV
+ * head from them.  With more than one chunk the per-chunk results are merged
+ * by log-sum-exp (kvd_merge_partials' arithmetic) inside the same call.
+ * With score set, adds score_weight * (1/n_q) * sum_h alpha_h(t) to
+ * score[i][t] for every t < s_i, alpha_h(t) being the softmax weight of
+ * token t for head h -- the per-layer term of the cumulative attention score
+ * (gist.science summary of "Not all thinking needs HBM", methodology 2); pass
+ * score_weight = 1/L to average over L layers.
+ * Returns KVD_ERR_DTYPE on an FP8 pool. */
+kvd_status kvd_decode_attn(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
+                           void* hip_stream);
+
+/* Same on an FP8 pool.  Codes are widened to bf16 in registers (exact) and
+ * the per-(block, head) scales are applied to the scores (K) and to the
+ * softmax weights (V), so no dense K/V is ever written back to memory (the
+ * no-reconstruction rule of the Spherical KV summary, §2.1).  Returns
+ * KVD_ERR_DTYPE on a bf16 pool. */
+kvd_status kvd_decode_attn_fp8(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
+                               void* hip_stream);
+
+/* Merge per-chunk partial results by log-sum-exp.
+ * part_o:   device fp32 [b][n_q][n_chunks][d_h], each chunk's normalised output
+ * part_lse: device fp32 [b][n_q][n_chunks], natural log; -inf marks an empty
+ *           chunk, which contributes nothing
+ * out_bf16: device bf16 [b][n_q][d_h]; lse_out: optional fp32 [b][n_q].
+ * lse = M + ln(sum_c exp(lse_c - M)), M = max_c lse_c, and
+ * out = sum_c exp(lse_c - lse) * o_c, rounded to bf16 (nearest even).
+ * d_h must be 64 or 128. */
+kvd_status kvd_merge_partials(const float* part_o, const float* part_lse, int32_t b, int32_t n_q,
+                              int32_t n_chunks, int32_t d_h, void* out_bf16, float* lse_out,
+                              void* hip_stream);
+
+/* Static string naming a status. */
+const char* kvd_status_string(kvd_status status);
+
+/* ---- test hooks: expose device-side pieces of the hot path ------------- */
+
+/* Element offsets (in elements of the pool's dtype, from kv_base) of K[t][c=0]
+ * and V[t][c=0] for every sequence i, KV head j and token t < n_tok, as the
+ * decode kernels compute them.  out_k, out_v: device int64 [b][n_kv][n_tok].
+ * Entries for table entries outside [0, num_blocks) are -1. */
+kvd_status kvd_debug_gather_offsets(const kvd_pool* pool, int32_t layer, const int32_t* block_table,
+                                    int32_t max_blocks_per_seq, int32_t b, int32_t n_tok,
+                                    int64_t* out_k, int64_t* out_v, void* hip_stream);
+
+/* Decode n E4M3 codes with the decode kernels' own widening routine.
+ * codes: device uint8 [n]; out: device fp32 [n]. */
+kvd_status kvd_debug_fp8_decode(const uint8_t* codes, int32_t n, float* out, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVDECODE_H */

@@ -68,11 +68,29 @@ def encode(y) -> np.ndarray:
     return (code.astype(np.int64) | sign).astype(np.uint8)
 
 
+def encode_nearest_even(y) -> np.ndarray:
+    """Same codes as :func:`encode`, computed with torch's float8_e4m3fn cast.
+
+    The cast rounds to nearest even but turns magnitudes past 464 into NaN, so
+    values are first clamped to +-448 (which is exactly what saturation asks
+    for).  It serves as a fast library step for large tensors; the tests pin it
+    to :func:`encode` on every code, every midpoint and random values.
+    """
+    import torch
+    y = np.clip(np.asarray(y, dtype=np.float32), -E4M3_MAX, E4M3_MAX)
+    return torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def scale_of_absmax(absmax):
+    """fp32 scale that maps a tile's absmax onto the largest code: absmax / 448."""
+    return (np.asarray(absmax, dtype=np.float32) / np.float32(E4M3_MAX)).astype(np.float32)
+
+
 def block_scale(x_rows) -> np.float32:
     """fp32 scale of one (block, head) tile: absmax over its filled rows / 448."""
     x = np.asarray(x_rows, dtype=np.float32)
     absmax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
-    return np.float32(absmax / np.float32(E4M3_MAX))
+    return np.float32(scale_of_absmax(absmax))
 
 
 def quantize_tile(x_rows, scale: np.float32) -> np.ndarray:
@@ -87,21 +105,24 @@ def quantize_sequence(X: np.ndarray):
     """Quantise one sequence's logical K (or V) ``[s][n_kv][d]``.
 
     Logical block ``b`` (tokens 16b .. 16b+15, the last one possibly short) of
-    KV head ``j`` gets one scale.  Returns codes ``[s][n_kv][d]`` (uint8) and
-    scales ``[n_blocks][n_kv]`` (float32).
+    KV head ``j`` gets one scale, the absmax of its filled rows over 448.
+    Returns codes ``[s][n_kv][d]`` (uint8) and scales ``[n_blocks][n_kv]``
+    (float32).  (Rows past the end are padded with zeros only to reshape; a
+    zero never raises an absmax.)
     """
     X = np.asarray(X, dtype=np.float32)
     s, n_kv, d = X.shape
     nb = -(-s // BLOCK_SIZE)
-    codes = np.zeros((s, n_kv, d), dtype=np.uint8)
-    scales = np.zeros((nb, n_kv), dtype=np.float32)
-    for b in range(nb):
-        lo, hi = b * BLOCK_SIZE, min(s, (b + 1) * BLOCK_SIZE)
-        for j in range(n_kv):
-            sc = block_scale(X[lo:hi, j, :])
-            scales[b, j] = sc
-            codes[lo:hi, j, :] = quantize_tile(X[lo:hi, j, :], sc)
-    return codes, scales
+    padded = np.zeros((nb * BLOCK_SIZE, n_kv, d), dtype=np.float32)
+    padded[:s] = X
+    tiles = padded.reshape(nb, BLOCK_SIZE, n_kv, d)
+    absmax = np.max(np.abs(tiles), axis=(1, 3))                   # [nb][n_kv], exact
+    scales = scale_of_absmax(absmax)                              # fp32 division
+    safe = np.where(scales == 0, np.float32(1), scales)
+    y = (tiles / safe[:, None, :, None]).astype(np.float32)       # fp32 division
+    codes = encode_nearest_even(y)
+    codes = np.where((scales == 0)[:, None, :, None], np.uint8(0), codes)
+    return codes.reshape(nb * BLOCK_SIZE, n_kv, d)[:s], scales
 
 
 def dequantize_sequence(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:

@@ -97,3 +97,20 @@ def gather(pool: np.ndarray, lay: PoolLayout, layer: int, table_row, s: int):
                 K[t, j, c] = pool[lay.k_offset(layer, p, j, row, c)]
                 V[t, j, c] = pool[lay.v_offset(layer, p, j, row, c)]
     return K, V
+
+
+def gather_indices(lay: PoolLayout, layer: int, table_row, s: int):
+    """Flat pool indices of a sequence's logical K and V, each ``[s][n_kv][d]``.
+
+    The same formulas as :meth:`PoolLayout.k_offset` / :meth:`v_offset`,
+    evaluated for all tokens, heads and channels at once.
+    """
+    t = np.arange(s, dtype=np.int64)
+    blk = np.asarray(table_row, dtype=np.int64)[t // BLOCK_SIZE]
+    row = t % BLOCK_SIZE
+    heads = np.arange(lay.n_kv, dtype=np.int64)
+    ch = np.arange(lay.head_dim, dtype=np.int64)
+    base = ((layer * lay.num_blocks + blk)[:, None] * lay.n_kv + heads[None, :]) * lay.tile_pair_elems
+    k_idx = base[:, :, None] + row[:, None, None] * lay.head_dim + ch[None, None, :]
+    v_idx = base[:, :, None] + BLOCK_SIZE * lay.head_dim + ch[None, None, :] * BLOCK_SIZE + row[:, None, None]
+    return k_idx, v_idx

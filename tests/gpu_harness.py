@@ -1,0 +1,161 @@
+"""Shared pieces of the GPU parity tests: build a paged case, run it, run the oracle.
+
+Inputs come from ``workloads`` (seeded, generated on the device by torch), are
+stored into the pool by ``kvd_write_kv`` and handed to the oracle in their
+logical, contiguous form; nothing the oracle sees comes from the HIP path.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import decode_attention_paged_04_amd as kvd
+import workloads as W
+from oracle import attention, e4m3, numerics, paged, scores
+
+DEV = "cuda"
+
+# Tolerances.  bf16 outputs are compared with the oracle rounded to bf16
+# (nearest even): max-abs 4e-3 and relative L2 1e-3 per output tensor of one
+# layer call.  FP8 pools: relative L2 1e-2 against the oracle run on the same
+# E4M3 codes.  Cumulative scores: 1e-5 relative per element.
+TOL_MAX_ABS = 4e-3
+TOL_REL_L2 = 1e-3
+TOL_FP8_REL_L2 = 1e-2
+TOL_SCORE_REL = 1e-5
+TOL_LSE = 1e-5
+
+
+def say(msg: str):
+    print(msg, flush=True)
+
+
+def bf16_to_f64(t) -> np.ndarray:
+    return numerics.bf16_bits_to_f64(t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def bf16_errors(got, ref_f64: np.ndarray):
+    """(max-abs, rel-L2) of bf16 ``got`` against the oracle rounded to bf16."""
+    g = bf16_to_f64(got)
+    r = numerics.round_to_bf16(ref_f64)
+    err = g - r
+    denom = np.linalg.norm(r)
+    rel = float(np.linalg.norm(err) / denom) if denom > 0 else float(np.linalg.norm(err))
+    return float(np.max(np.abs(err))) if err.size else 0.0, rel
+
+
+def assert_bf16_close(got, ref_f64, rel_tol=TOL_REL_L2, what=""):
+    mx, rel = bf16_errors(got, ref_f64)
+    assert mx <= TOL_MAX_ABS and rel <= rel_tol, f"{what}: max-abs {mx:.3g}, rel-L2 {rel:.3g}"
+    return mx, rel
+
+
+def assert_lse_close(got, ref):
+    g = got.detach().cpu().double().numpy()
+    both_inf = np.isneginf(g) & np.isneginf(ref)
+    fin = ~both_inf
+    assert np.all(np.isfinite(g[fin])) and np.all(np.isfinite(ref[fin]))
+    if fin.any():
+        err = np.abs(g[fin] - ref[fin]) / np.maximum(1.0, np.abs(ref[fin]))
+        assert float(np.max(err)) <= TOL_LSE, f"lse error {np.max(err):.3g}"
+
+
+class PagedCase:
+    """A seeded batch stored in a paged pool, plus what the oracle needs."""
+
+    def __init__(self, w: W.DecodeWorkload, layers: int = None, lens=None, table=None,
+                 num_blocks: int = None, poison: bool = True, keep_layers=None, keep_seqs=None):
+        self.w = w
+        self.L = layers if layers is not None else w.layers
+        self.lens = np.asarray(lens if lens is not None else W.context_lengths(w), dtype=np.int32)
+        if table is None:
+            table, nb = W.block_tables(w, self.lens)
+        else:
+            nb = num_blocks
+        self.table = np.asarray(table, dtype=np.int32)
+        self.num_blocks = int(nb)
+        self.fp8 = w.kv_dtype == "fp8"
+        dt = kvd.KVD_FP8_E4M3 if self.fp8 else kvd.KVD_BF16
+        self.pool = kvd.allocate_pool(self.L, self.num_blocks, w.n_kv, w.head_dim, dt)
+        if poison:
+            self.pool.kv.fill_(0xFF)          # NaN in every bf16 / E4M3 slot never written
+        self.lens_t = torch.from_numpy(self.lens).to(DEV)
+        self.table_t = torch.from_numpy(self.table).to(DEV)
+        self.max_ctx = int(self.lens.max()) if len(self.lens) else 0
+        self.offs = W.offsets(self.lens)
+        slots = kvd.slot_mapping_for(self.table_t, self.lens_t)
+        keep = set(range(self.L)) if keep_layers is None else set(keep_layers)
+        self.keep_seqs = None if keep_seqs is None else sorted(set(int(i) for i in keep_seqs))
+        self.q, self.kv, self.kv_seq = {}, {}, {}
+        n = int(self.offs[-1])
+        for layer in range(self.L):
+            q = W.query(w, layer, DEV)
+            K, V = W.keys_values(w, layer, n, DEV)
+            kvd.kvd_write_kv(self.pool, layer, K, V, slots)
+            self.q[layer] = q
+            if layer in keep:
+                if self.keep_seqs is None:
+                    self.kv[layer] = (K.cpu(), V.cpu())
+                else:
+                    for i in self.keep_seqs:
+                        lo, hi = int(self.offs[i]), int(self.offs[i + 1])
+                        self.kv_seq[(layer, i)] = (K[lo:hi].cpu(), V[lo:hi].cpu())
+            del K, V
+        torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- GPU
+    def run(self, layer: int, chunk: int = 0, score=None, weight: float = 0.0, lse: bool = True):
+        q = self.q[layer]
+        out = torch.empty_like(q)
+        lse_out = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV) if lse else None
+        kvd.decode(self.pool, layer, q, self.table_t, self.lens_t, self.max_ctx, out=out,
+                   lse_out=lse_out, chunk_tokens=chunk, score=score, score_weight=weight)
+        return out, lse_out
+
+    # ---------------------------------------------------------------- oracle
+    def logical(self, layer: int, i: int):
+        """float64 K, V ``[s][n_kv][d]`` of sequence i as the oracle sees them."""
+        if (layer, i) in self.kv_seq:
+            Ks, Vs = self.kv_seq[(layer, i)]
+        else:
+            K, V = self.kv[layer]
+            lo, hi = int(self.offs[i]), int(self.offs[i + 1])
+            Ks, Vs = K[lo:hi], V[lo:hi]
+        Kf = bf16_to_f64(Ks)
+        Vf = bf16_to_f64(Vs)
+        if self.fp8:
+            ck, sk = e4m3.quantize_sequence(Kf.astype(np.float32))
+            cv, sv = e4m3.quantize_sequence(Vf.astype(np.float32))
+            return e4m3.dequantize_sequence(ck, sk), e4m3.dequantize_sequence(cv, sv)
+        return Kf, Vf
+
+    def oracle(self, layer: int, seqs=None):
+        if seqs is None:
+            seqs = range(len(self.lens)) if self.keep_seqs is None else self.keep_seqs
+        qf = bf16_to_f64(self.q[layer])
+        o = np.zeros(qf.shape)
+        lse = np.full(qf.shape[:2], -np.inf)
+        for i in seqs:
+            K, V = self.logical(layer, i)
+            o[i], lse[i] = attention.decode_sequence(qf[i], K, V)
+        return o, lse
+
+    def oracle_alpha(self, layer: int, i: int):
+        K, _ = self.logical(layer, i)
+        return attention.attention_weights_sequence(bf16_to_f64(self.q[layer])[i], K)
+
+    def oracle_scores(self, init: np.ndarray, seqs, weight: float):
+        ref = init.astype(np.float64).copy()
+        for i in seqs:
+            s = int(self.lens[i])
+            for layer in range(self.L):
+                if s:
+                    ref[i, :s] += scores.layer_increment(self.oracle_alpha(layer, i), weight)
+        return ref
+
+    def layout(self):
+        return paged.PoolLayout(self.L, self.num_blocks, self.w.n_kv, self.w.head_dim)
+
+
+def score_rel_error(got: np.ndarray, ref: np.ndarray) -> float:
+    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-30))) if got.size else 0.0

@@ -102,7 +102,11 @@ def e4m3_encode_mismatches(n=200_000, seed=1) -> int:
     ])
     ours = e4m3.encode(x)
     theirs = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    return int(np.count_nonzero(ours != theirs))
+    # the fast path the quantiser uses must agree too, saturation included
+    wide = np.concatenate([x, np.array([464.0, 465.0, 1e30, -1e30, np.inf, -np.inf], np.float32),
+                           (rng.uniform(-1e4, 1e4, n)).astype(np.float32)])
+    fast_bad = np.count_nonzero(e4m3.encode_nearest_even(wide) != e4m3.encode(wide))
+    return int(np.count_nonzero(ours != theirs)) + int(fast_bad)
 
 
 def e4m3_page_fact_failures() -> list:

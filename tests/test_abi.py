@@ -1,0 +1,182 @@
+"""The C ABI on the host: exports, pool sizing, validation and planning (no GPU).
+
+None of these calls reach a kernel launch: every argument error is detected on
+the host first, and the pool / plan functions are pure host code.  Device
+pointers are stand-in integers that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_paged_04_amd as kvd
+from oracle import footprint
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 24            # 16-byte aligned stand-in for a device pointer
+
+
+def header_symbols():
+    hdr = open(os.path.join(ROOT, "include", "kvdecode.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvd_[a-z0-9_]+)\s*\(", hdr)))
+
+
+def test_every_declared_symbol_is_exported():
+    syms = header_symbols()
+    assert "kvd_decode_attn" in syms and "kvd_merge_partials" in syms
+    lib = ctypes.CDLL(kvd.LIB_PATH)
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert set(syms) == set(kvd.EXPORTS), "binding and header disagree"
+
+
+@pytest.mark.parametrize("layers,n_kv,d,dtype,per_token", [
+    (32, 8, 128, kvd.KVD_BF16, 131072),        # Llama-3.1-8B, BF16
+    (80, 8, 128, kvd.KVD_BF16, 327680),        # Llama-3(.1)-70B, BF16
+    (32, 8, 128, kvd.KVD_FP8_E4M3, 65536),     # 8B with FP8 KV
+])
+def test_pool_bytes_per_token(layers, n_kv, d, dtype, per_token):
+    kv, sc = kvd.kvd_pool_bytes(layers, 100, n_kv, d, dtype)
+    assert kv / (100 * 16) == per_token
+    w = 2 if dtype == kvd.KVD_BF16 else 1
+    assert kv / (100 * 16) == footprint.kv_bytes_per_token(layers, n_kv, d, w)
+    assert sc == (layers * 100 * n_kv * 2 * 4 if dtype == kvd.KVD_FP8_E4M3 else 0)
+
+
+def _status(fn, *args):
+    return getattr(kvd.lib, fn)(*args)
+
+
+def _desc(**kw):
+    base = dict(num_layers=2, num_blocks=64, block_size=16, n_kv=2, head_dim=128, dtype=kvd.KVD_BF16)
+    base.update(kw)
+    return kvd.PoolDesc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_size=32), 2), (dict(head_dim=96), 2), (dict(head_dim=256), 2),
+    (dict(num_layers=0), 1), (dict(num_blocks=0), 1), (dict(n_kv=0), 1), (dict(dtype=7), 1),
+    (dict(num_blocks=1 << 18, n_kv=8), 2),         # one layer >= 4 GiB
+])
+def test_pool_desc_errors(kw, status):
+    d = _desc(**kw)
+    h = ctypes.c_void_p(0)
+    assert _status("kvd_create_pool", ctypes.byref(d), FAKE, None, ctypes.byref(h)) == status
+    assert not h.value
+
+
+def test_create_pool_pointer_rules():
+    h = ctypes.c_void_p(0)
+    d = _desc()
+    assert _status("kvd_create_pool", ctypes.byref(d), None, None, ctypes.byref(h)) == 1
+    assert _status("kvd_create_pool", ctypes.byref(d), FAKE + 8, None, ctypes.byref(h)) == 1
+    assert _status("kvd_create_pool", ctypes.byref(d), FAKE, FAKE, ctypes.byref(h)) == 1   # bf16 + scales
+    d8 = _desc(dtype=kvd.KVD_FP8_E4M3)
+    assert _status("kvd_create_pool", ctypes.byref(d8), FAKE, None, ctypes.byref(h)) == 1  # fp8, no scales
+    assert _status("kvd_create_pool", ctypes.byref(d8), FAKE, FAKE, None) == 1
+    assert _status("kvd_create_pool", ctypes.byref(d8), FAKE, FAKE, ctypes.byref(h)) == 0
+    assert _status("kvd_destroy_pool", h) == 0
+    assert _status("kvd_destroy_pool", None) == 1
+
+
+def _pool(dtype=kvd.KVD_BF16, head_dim=128, n_kv=2):
+    d = _desc(dtype=dtype, head_dim=head_dim, n_kv=n_kv)
+    h = ctypes.c_void_p(0)
+    assert _status("kvd_create_pool", ctypes.byref(d), FAKE,
+                   FAKE if dtype == kvd.KVD_FP8_E4M3 else None, ctypes.byref(h)) == 0
+    return kvd.Pool(d, None, None, h.value)
+
+
+def _args(**kw):
+    base = dict(b=2, n_q=8, max_blocks_per_seq=8, max_context_len=100, q=FAKE, block_table=FAKE,
+                context_lens=FAKE, out=FAKE, lse_out=None, chunk_tokens=0, workspace=None,
+                workspace_bytes=0, score=None, score_stride=0, score_weight=0.0)
+    base.update(kw)
+    return kvd.DecodeArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q=7), 1),                      # n_q not a multiple of n_kv
+    (dict(n_q=34), 2),                     # g = 17 > 16
+    (dict(chunk_tokens=24), 1),            # not a multiple of 16
+    (dict(chunk_tokens=-16), 1),
+    (dict(b=-1), 1), (dict(max_blocks_per_seq=0), 1), (dict(max_context_len=-5), 1),
+    (dict(q=None), 1), (dict(block_table=None), 1), (dict(context_lens=None), 1), (dict(out=None), 1),
+    (dict(score=FAKE, score_stride=50), 1),      # stride shorter than the context bound
+    (dict(chunk_tokens=16), 4),            # needs a workspace, none given
+    (dict(chunk_tokens=16, workspace=FAKE, workspace_bytes=16), 4),
+    (dict(chunk_tokens=16, workspace=FAKE + 16, workspace_bytes=1 << 30), 4),   # misaligned
+])
+def test_decode_argument_errors(kw, status):
+    pool = _pool()
+    a = _args(**kw)
+    assert _status("kvd_decode_attn", pool.handle, 0, ctypes.byref(a), None) == status
+
+
+def test_decode_dtype_and_layer_errors():
+    bf, f8 = _pool(), _pool(kvd.KVD_FP8_E4M3)
+    a = _args()
+    assert _status("kvd_decode_attn_fp8", bf.handle, 0, ctypes.byref(a), None) == 3
+    assert _status("kvd_decode_attn", f8.handle, 0, ctypes.byref(a), None) == 3
+    assert _status("kvd_decode_attn", bf.handle, 2, ctypes.byref(a), None) == 1
+    assert _status("kvd_decode_attn", bf.handle, -1, ctypes.byref(a), None) == 1
+    assert _status("kvd_decode_attn", None, 0, ctypes.byref(a), None) == 1
+    assert _status("kvd_decode_attn", bf.handle, 0, None, None) == 1
+    # an empty batch is a valid no-op
+    a0 = _args(b=0)
+    assert _status("kvd_decode_attn", bf.handle, 0, ctypes.byref(a0), None) == 0
+
+
+def test_write_and_merge_argument_errors():
+    pool = _pool()
+    assert _status("kvd_write_kv", pool.handle, 5, FAKE, FAKE, FAKE, 4, None) == 1
+    assert _status("kvd_write_kv", pool.handle, 0, FAKE, FAKE, FAKE, -1, None) == 1
+    assert _status("kvd_write_kv", pool.handle, 0, None, FAKE, FAKE, 4, None) == 1
+    assert _status("kvd_write_kv", pool.handle, 0, None, None, None, 0, None) == 0
+    assert _status("kvd_merge_partials", FAKE, FAKE, 1, 4, 2, 96, FAKE, None, None) == 2
+    assert _status("kvd_merge_partials", FAKE, FAKE, 1, 4, 0, 128, FAKE, None, None) == 1
+    assert _status("kvd_merge_partials", None, FAKE, 1, 4, 2, 128, FAKE, None, None) == 1
+    assert _status("kvd_merge_partials", None, None, 0, 4, 2, 128, None, None, None) == 0
+    assert _status("kvd_debug_fp8_decode", None, -1, None, None) == 1
+    assert _status("kvd_debug_gather_offsets", pool.handle, 0, FAKE, 2, 1, 33, FAKE, FAKE, None) == 1
+
+
+def _plan(pool, **kw):
+    a = _args(**kw)
+    c, n = kvd.kvd_decode_plan(pool, a)
+    ws = kvd.kvd_decode_workspace_bytes(pool, a)
+    return c, n, ws
+
+
+def test_plan_and_workspace():
+    pool = _pool()
+    # forced chunks: ceil(100 / 32) = 4 chunks; partials b*n_q*4*(128+1) fp32, each region 256-aligned
+    c, n, ws = _plan(pool, chunk_tokens=32)
+    assert (c, n) == (32, 4)
+    po = 2 * 8 * 4 * 128 * 4
+    pl = -(-(2 * 8 * 4 * 4) // 256) * 256
+    assert ws == po + pl
+    # one chunk and no score: no workspace
+    c, n, ws = _plan(pool, chunk_tokens=0, max_context_len=100)
+    assert n == 1 and ws == 0 and c >= 100
+    # scores add the logit scratch and the lse buffer
+    c, n, ws = _plan(pool, score=FAKE, score_stride=100)
+    stride = (100 + 31) // 32 * 32 + 32
+    assert ws == -(-(2 * 8 * stride * 4) // 256) * 256 + 256
+    # the context bound is clamped by the block table width
+    c, n, _ = _plan(pool, chunk_tokens=16, max_context_len=1000)
+    assert n == 8
+
+
+@pytest.mark.parametrize("b,n_kv,n_q,s", [(1, 8, 32, 32768), (4, 8, 64, 131072), (32, 8, 32, 16384)])
+def test_auto_plan_fills_the_chip(b, n_kv, n_q, s):
+    d = _desc(n_kv=n_kv, num_blocks=1024)
+    h = ctypes.c_void_p(0)
+    assert _status("kvd_create_pool", ctypes.byref(d), FAKE, None, ctypes.byref(h)) == 0
+    pool = kvd.Pool(d, None, None, h.value)
+    a = _args(b=b, n_q=n_q, max_context_len=s, max_blocks_per_seq=s // 16)
+    c, n = kvd.kvd_decode_plan(pool, a)
+    assert c % 16 == 0 and n == -(-s // c)
+    assert b * n_kv * n >= 512          # at least two workgroups per compute unit

@@ -1,0 +1,106 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark times.
+
+The per-layer launch (grid, chunking, workspace) is the benchmark's; where a
+workload has many layers the pool keeps two of them (layer 1 is checked, so
+the layer offset is not zero), except the FP8 + score workload, whose
+cumulative score needs every layer.  Outputs are sampled by sequence where
+the float64 oracle would take too long for all of them.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import decode_attention_paged_04_amd as kvd
+    import gpu_harness as H
+    import workloads as W
+    return kvd, H, W, torch
+
+
+def _check(H, torch, case, layer, seqs=None, rel_tol=None):
+    out, lse = case.run(layer)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = case.oracle(layer, seqs)
+    seqs = list(range(len(case.lens))) if seqs is None else list(seqs)
+    for i in seqs:
+        mx, rel = H.assert_bf16_close(out[i], ref_o[i], rel_tol=rel_tol or H.TOL_REL_L2,
+                                      what=f"{case.w.name} layer {layer} seq {i}")
+        H.say(f"{case.w.name} layer {layer} seq {i}: max-abs {mx:.2e} rel-L2 {rel:.2e}")
+    H.assert_lse_close(lse[seqs], ref_lse[seqs])
+
+
+def test_full_8b_single_layer(env):
+    kvd, H, W, torch = env
+    case = H.PagedCase(W.WORKLOADS["8b_layer"])
+    _check(H, torch, case, 0)
+
+
+def test_full_8b_ragged_batch(env):
+    kvd, H, W, torch = env
+    w = W.WORKLOADS["8b_ragged"]
+    case = H.PagedCase(w, layers=2, keep_layers=[1])
+    _check(H, torch, case, 1)
+
+
+def test_full_70b_long_context(env):
+    kvd, H, W, torch = env
+    w = W.WORKLOADS["70b_long"]
+    case = H.PagedCase(w, layers=2, keep_layers=[1], keep_seqs=[0, 3])
+    _check(H, torch, case, 1, seqs=[0, 3])
+
+
+def test_full_8b_fp8_with_scores(env):
+    kvd, H, W, torch = env
+    from oracle import e4m3, paged
+    w = W.WORKLOADS["8b_fp8_scores"]
+    lens = W.context_lengths(w)
+    rng = np.random.default_rng(w.seed + 77)
+    seqs = sorted({int(np.argmin(lens)), int(rng.integers(0, w.b))})
+    H.say(f"fp8+scores: sampled sequences {seqs} of lengths {[int(lens[i]) for i in seqs]}")
+    case = H.PagedCase(w, keep_seqs=seqs)
+    stride = case.max_ctx
+    init = W.initial_scores(w, stride, "cuda")
+    score = init.clone()
+    init_np = init.cpu().numpy()
+    outs = {}
+    for layer in range(w.layers):
+        out, lse = case.run(layer, score=score, weight=1.0 / w.layers)
+        if layer in (0, w.layers - 1):
+            outs[layer] = (out.clone(), lse.clone())
+    torch.cuda.synchronize()
+    for layer, (out, lse) in outs.items():
+        ref_o, ref_lse = case.oracle(layer, seqs)
+        for i in seqs:
+            mx, rel = H.assert_bf16_close(out[i], ref_o[i], rel_tol=H.TOL_FP8_REL_L2,
+                                          what=f"fp8 layer {layer} seq {i}")
+            H.say(f"fp8 layer {layer} seq {i}: max-abs {mx:.2e} rel-L2 {rel:.2e}")
+        H.assert_lse_close(lse[seqs], ref_lse[seqs])
+    # the stored codes and scales of the sampled sequences, layer 5
+    lay = case.layout()
+    for i in seqs:
+        s = int(lens[i])
+        k_idx, v_idx = paged.gather_indices(lay, 5, case.table[i], s)
+        Ks, Vs = case.kv_seq[(5, i)]
+        ck, sk = e4m3.quantize_sequence(Ks.float().numpy())
+        cv, sv = e4m3.quantize_sequence(Vs.float().numpy())
+        kv = case.pool.kv
+        got_k = kv[torch.from_numpy(k_idx).cuda()].cpu().numpy()
+        got_v = kv[torch.from_numpy(v_idx).cuda()].cpu().numpy()
+        assert np.array_equal(got_k, ck) and np.array_equal(got_v, cv)
+        nb = sk.shape[0]
+        sc_idx = np.array([[lay.scale_index(5, int(case.table[i, b]), j, 0) for j in range(w.n_kv)]
+                           for b in range(nb)])
+        got_sk = case.pool.scales[torch.from_numpy(sc_idx).cuda()].cpu().numpy()
+        got_sv = case.pool.scales[torch.from_numpy(sc_idx + 1).cuda()].cpu().numpy()
+        assert np.array_equal(got_sk, sk) and np.array_equal(got_sv, sv)
+    got = score.cpu().double().numpy()
+    ref = case.oracle_scores(init_np, seqs, 1.0 / w.layers)
+    for i in seqs:
+        err = H.score_rel_error(got[i], ref[i])
+        H.say(f"scores seq {i}: max rel error {err:.2e}")
+        assert err <= H.TOL_SCORE_REL

@@ -104,9 +104,8 @@ def _step_inc_no_head_mean(alphas):
     return acc / len(alphas)
 
 
-def _scale_over_256(x_rows):
-    x = np.asarray(x_rows, dtype=np.float32)
-    return np.float32(np.float32(np.max(np.abs(x))) / np.float32(256.0))
+def _scale_over_256(absmax):
+    return (np.asarray(absmax, dtype=np.float32) / np.float32(256.0)).astype(np.float32)
 
 
 MUTATIONS = [
@@ -122,7 +121,7 @@ MUTATIONS = [
     ("slot off by one", paged, "slot", _slot_off_by_one),
     ("score missing head mean", scores, "layer_increment", _layer_inc_no_head_mean),
     ("score step missing head mean", scores, "step_increment", _step_inc_no_head_mean),
-    ("fp8 scale absmax/256", e4m3, "block_scale", _scale_over_256),
+    ("fp8 scale absmax/256", e4m3, "scale_of_absmax", _scale_over_256),
 ]
 
 

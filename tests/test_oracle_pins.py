@@ -131,3 +131,16 @@ def test_brute_force_grid(g, d):
             torch.from_numpy(q)[None, :, None], torch.from_numpy(K).permute(1, 0, 2)[None],
             torch.from_numpy(V).permute(1, 0, 2)[None], enable_gqa=True)[0, :, 0].numpy()
         assert np.max(np.abs(o - ref)) < 1e-13
+
+
+def test_vectorised_gather_indices_match_scalar_layout():
+    from oracle import paged
+    lay = paged.PoolLayout(num_layers=3, num_blocks=9, n_kv=2, head_dim=8)
+    table = [4, 0, 7]
+    k_idx, v_idx = paged.gather_indices(lay, 2, table, 37)
+    for t in (0, 5, 15, 16, 31, 36):
+        p, row = divmod(paged.slot(table, t), 16)
+        for j in range(2):
+            for c in (0, 3, 7):
+                assert k_idx[t, j, c] == lay.k_offset(2, p, j, row, c)
+                assert v_idx[t, j, c] == lay.v_offset(2, p, j, row, c)
