@@ -1,0 +1,380 @@
+#!/usr/bin/env python3
+"""Benchmark of paged GQA decode attention on one MI355X (gfx950).
+
+One *step* is one decode step of the whole batch through every layer of the
+workload: one libkvdecode decode call per layer, each streaming that layer's
+cached K/V once.  The headline workload is the Llama-3.1-8B-shaped single
+layer (b = 1, 32 query / 8 KV heads, head dim 128, s = 32,768); the
+Llama-3-70B-shaped long-context step (b = 4, 80 layers, s = 131,072, about
+172 GB of resident KV) is reported beside it.
+
+Reported:
+* value       -- algorithmic KV GB/s of the whole step (bytes the method must
+                 move, see ``algorithmic_step_bytes``) over wall time of
+                 exactly K steps bracketed by device synchronisation;
+* seq-steps/s -- sequences x steps per second; % of the 8 TB/s HBM peak;
+* roofline    -- the decode kernel alone: algorithmic bytes per launch over
+                 its mean duration from a HIP event pair around every launch;
+* cpu_baseline-- the float64 oracle timed on a bounded sample on the host.
+
+Timing details: inputs are resident in HBM before the timed region; the step
+sequence is captured in HIP graphs (one launch per layer call) and replayed,
+so host launch overhead does not pace the ~20 us single-layer step; when one
+step's bytes would fit the 256 MB Infinity Cache, several replicas of the
+pool are stepped through in turn so that every step reads from HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn KV GB/s (% of HBM peak) + seq-steps/s, 8B & 70B GQA shapes"
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
+INFINITY_CACHE_BYTES = 256 << 20
+HEADLINE = "8b_layer"
+SECONDARY = "70b_long"
+DECODE_SOURCES = ["decode.hip", "device_common.h", "kvd_internal.h"]
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_step_bytes(lens, layers, n_q, n_kv, head_dim, kv_bytes, fp8, scores) -> int:
+    """Bytes one step must move (per layer: every cached K/V element once, q in
+    and the bf16 output out, one 4-byte block id per block, two fp32 scales per
+    (block, KV head) for FP8; a score update reads and writes 4 bytes per token
+    once per step).  Implementation scratch (partials, score scratch) and the
+    unused rows of a partly filled last block are not counted."""
+    total = 0
+    for s in lens:
+        s = int(s)
+        nblk = -(-s // 16)
+        per_layer = 2 * n_kv * head_dim * kv_bytes * s + 2 * n_q * head_dim * 2 + 4 * nblk
+        if fp8:
+            per_layer += 2 * n_kv * 4 * nblk
+        total += layers * per_layer + (8 * s if scores else 0)
+    return total
+
+
+class Workload:
+    """A workload resident in HBM, ready to be stepped (eagerly or from graphs)."""
+
+    def __init__(self, name: str, chunk: int, replicas: int):
+        import torch
+        import decode_attention_paged_04_amd as kvd
+        import workloads as W
+
+        self.kvd, self.torch = kvd, torch
+        self.w = w = W.WORKLOADS[name]
+        self.fp8 = w.kv_dtype == "fp8"
+        self.lens = W.context_lengths(w)
+        self.table, self.num_blocks = W.block_tables(w, self.lens)
+        self.max_ctx = int(self.lens.max())
+        self.kv_bytes = 1 if self.fp8 else 2
+        self.step_bytes = algorithmic_step_bytes(self.lens, w.layers, w.n_q, w.n_kv, w.head_dim,
+                                                 self.kv_bytes, self.fp8, w.scores)
+        self.launch_bytes = algorithmic_step_bytes(self.lens, 1, w.n_q, w.n_kv, w.head_dim,
+                                                   self.kv_bytes, self.fp8, False)
+        if replicas <= 0:
+            replicas = max(1, math.ceil(4 * INFINITY_CACHE_BYTES / self.step_bytes))
+        self.R = replicas
+        dev = "cuda"
+        self.lens_t = torch.from_numpy(self.lens).to(dev)
+        self.table_t = torch.from_numpy(self.table).to(dev)
+        slots = kvd.slot_mapping_for(self.table_t, self.lens_t)
+        n_tok = int(self.lens.sum())
+        dt = kvd.KVD_FP8_E4M3 if self.fp8 else kvd.KVD_BF16
+        t0 = time.time()
+        self.pools = [kvd.allocate_pool(w.layers, self.num_blocks, w.n_kv, w.head_dim, dt)
+                      for _ in range(self.R)]
+        self.q = []
+        for layer in range(w.layers):
+            K, V = W.keys_values(w, layer, n_tok, dev)
+            for p in self.pools:
+                kvd.kvd_write_kv(p, layer, K, V, slots)
+            self.q.append(W.query(w, layer, dev))
+            del K, V
+        torch.cuda.synchronize()
+        log(f"{w.name}: {self.R} pool(s) of {self.pools[0].kv.numel() / 1e9:.2f} GB filled in "
+            f"{time.time() - t0:.1f}s")
+        self.out = [torch.empty_like(q) for q in self.q]
+        self.score = None
+        if w.scores:
+            self.score0 = W.initial_scores(w, self.max_ctx, dev)
+            self.score = self.score0.clone()
+        probe = kvd.make_args(self.q[0], self.table_t, self.lens_t, self.max_ctx, self.out[0],
+                              chunk_tokens=chunk, score=self.score,
+                              score_weight=1.0 / w.layers, pool=self.pools[0])
+        self.chunk, self.n_chunks = kvd.kvd_decode_plan(self.pools[0], probe)
+        ws_bytes = kvd.kvd_decode_workspace_bytes(self.pools[0], probe)
+        self.ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.args = [[kvd.make_args(self.q[l], self.table_t, self.lens_t, self.max_ctx, self.out[l],
+                                    chunk_tokens=chunk, workspace=self.ws, score=self.score,
+                                    score_weight=1.0 / w.layers, pool=self.pools[r])
+                      for l in range(w.layers)] for r in range(self.R)]
+        self.fn = kvd.lib.kvd_decode_attn_fp8 if self.fp8 else kvd.lib.kvd_decode_attn
+        # the decode kernel on its own: per-chunk partials into separate buffers
+        b, n_q, d = w.b, w.n_q, w.head_dim
+        self.part_o = torch.empty((b, n_q, self.n_chunks, d), dtype=torch.float32, device=dev)
+        self.part_lse = torch.empty((b, n_q, self.n_chunks), dtype=torch.float32, device=dev)
+        self.pargs = [[kvd.make_args(self.q[l], self.table_t, self.lens_t, self.max_ctx, None,
+                                     chunk_tokens=chunk, pool=self.pools[r], need_out=False)
+                       for l in range(w.layers)] for r in range(self.R)]
+
+    def call(self, r: int, layer: int, stream: int):
+        st = self.fn(self.pools[r].handle, layer, ctypes.byref(self.args[r][layer]), stream)
+        if st != 0:
+            raise RuntimeError(f"decode call failed: {self.kvd.kvd_status_string(st)}")
+
+    def call_partials(self, r: int, layer: int, stream: int):
+        st = self.kvd.lib.kvd_decode_partials(self.pools[r].handle, layer, ctypes.byref(self.pargs[r][layer]),
+                                              self.part_o.data_ptr(), self.part_lse.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError(f"partials call failed: {self.kvd.kvd_status_string(st)}")
+
+    def step(self, r: int):
+        stream = int(self.torch.cuda.current_stream().cuda_stream)
+        for layer in range(self.w.layers):
+            self.call(r, layer, stream)
+
+    def capture(self):
+        """One graph per replica (one step each) and one graph stepping all replicas."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in range(self.R):
+                self.step(r)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.single = []
+        for r in range(self.R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(r)
+            self.single.append(g)
+        self.all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.all):
+            for r in range(self.R):
+                self.step(r)
+        torch.cuda.synchronize()
+
+    def run_steps(self, k: int):
+        """Exactly k steps: full rotations from one graph, the rest one by one."""
+        full, rest = divmod(k, self.R)
+        for _ in range(full):
+            self.all.replay()
+        for r in range(rest):
+            self.single[r].replay()
+
+    def time_steps(self, steps: int, warmup: int) -> float:
+        torch = self.torch
+        self.run_steps(warmup)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        self.run_steps(steps)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def time_launches(self, n: int) -> float:
+        """Mean duration (s) of the decode kernel, from a HIP event pair around each
+        launch (a kvd_decode_partials call is exactly one launch of it)."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        h = int(stream.cuda_stream)
+        evs = []
+        for k in range(n):
+            r, layer = k % self.R, (k // self.R) % self.w.layers
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            self.call_partials(r, layer, h)
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / len(evs) / 1e3
+
+    def config(self):
+        w = self.w
+        ctx = (str(int(w.ctx[1])) if w.ctx[0] == "fixed"
+               else f"U[{w.ctx[1]},{w.ctx[2]}] (sum {int(self.lens.sum())})")
+        return {"workload": w.name, "b": w.b, "layers": w.layers, "n_q": w.n_q, "n_kv": w.n_kv,
+                "head_dim": w.head_dim, "context": ctx, "block_size": 16,
+                "kv_dtype": w.kv_dtype, "fused_scores": bool(w.scores),
+                "chunk_tokens": self.chunk, "n_chunks": self.n_chunks, "pool_replicas": self.R,
+                "num_blocks": self.num_blocks, "hip_graphs": True}
+
+    def free(self):
+        torch = self.torch
+        del self.pools, self.args, self.pargs, self.q, self.out, self.ws, self.part_o, self.part_lse
+        if hasattr(self, "single"):
+            del self.single, self.all
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_paged_04_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current decode kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"decode kernel source digest:\s*`?([0-9a-f]+)", txt)
+    m_b = re.search(r"HBM bytes per launch \(calibrated\):\s*([0-9.eE+]+)", txt)
+    if not m_src or not m_b or m_src.group(1) != source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(wl: Workload, budget_s: float):
+    """The float64 oracle as it stands, timed on the host on a bounded sample."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from oracle import attention, numerics
+
+    def f64(t):
+        return numerics.bf16_bits_to_f64(t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+    w = wl.w
+    i = 0
+    s = int(wl.lens[i])
+    K, V = W.keys_values(w, 0, int(wl.lens.sum()), "cuda")
+    Kf, Vf = f64(K[:s]), f64(V[:s])
+    del K, V
+    qf = f64(wl.q[0])[i]
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        attention.decode_sequence(qf, Kf, Vf)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    seq_layer_bytes = algorithmic_step_bytes([s], 1, w.n_q, w.n_kv, w.head_dim, wl.kv_bytes, wl.fp8, False)
+    return {"value": round(seq_layer_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"oracle decode of sequence {i} for one layer ({w.n_q} query heads, s={s}, "
+                       f"float64 numpy) repeated {reps}x in {reps * dt:.1f}s; host cores visible: "
+                       f"{len(os.sched_getaffinity(0))}"),
+            "seq_layer_steps_per_s": round(1.0 / dt, 3)}
+
+
+def measure(name: str, chunk: int, replicas: int, steps: int, warmup: int, launches: int):
+    wl = Workload(name, chunk, replicas)
+    wl.capture()
+    secs = wl.time_steps(steps, warmup)
+    ms = secs / steps * 1e3
+    launch_s = wl.time_launches(launches)
+    achieved = wl.launch_bytes / launch_s / 1e9
+    value = wl.step_bytes / (secs / steps) / 1e9
+    res = {"value": value, "ms_per_step": ms, "seq_steps_per_s": wl.w.b * steps / secs,
+           "pct_of_hbm_peak": 100.0 * value / PEAK_HBM_GBS, "step_bytes": wl.step_bytes,
+           "launch_bytes": wl.launch_bytes, "launch_us": launch_s * 1e6, "achieved": achieved,
+           "config": wl.config()}
+    log(f"{name}: {ms:.4f} ms/step, {value:.1f} GB/s ({res['pct_of_hbm_peak']:.1f}% of peak), "
+        f"decode launch {launch_s * 1e6:.2f} us -> {achieved:.1f} GB/s")
+    return wl, res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--secondary", default=SECONDARY, help="second workload in the same line, or 'none'")
+    ap.add_argument("--secondary-steps", type=int, default=10)
+    ap.add_argument("--chunk", type=int, default=0, help="chunk_tokens (0 = the library's choice)")
+    ap.add_argument("--replicas", type=int, default=0, help="pool replicas (0 = enough to exceed the cache)")
+    ap.add_argument("--launches", type=int, default=200, help="event-timed launches for the roofline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the decode step "
+              f"shards by sequence or KV head with no exchange, so N GPUs run N independent copies).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    wl, head = measure(args.workload, args.chunk, args.replicas, args.steps, args.warmup, args.launches)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        log(f"cpu baseline: {cpu['value']} GB/s on {cpu['cores']} thread(s)")
+    wl.free()
+    del wl
+
+    secondary = None
+    if args.secondary != "none" and args.secondary != args.workload:
+        wl2, sec = measure(args.secondary, 0, 0, args.secondary_steps, 2, 80)
+        wl2.free()
+        del wl2
+        traffic2 = measured_traffic(args.secondary)
+        secondary = {"workload": sec["config"]["workload"], "value": round(sec["value"], 2), "unit": "GB/s",
+                     "ms_per_step": round(sec["ms_per_step"], 4), "steps": args.secondary_steps,
+                     "seq_steps_per_s": round(sec["seq_steps_per_s"], 3),
+                     "pct_of_hbm_peak": round(sec["pct_of_hbm_peak"], 2), "config": sec["config"],
+                     "roofline": {"bound": "hbm", "achieved": round(sec["achieved"], 2),
+                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(sec["achieved"] / PEAK_HBM_GBS, 4),
+                                  "traffic": traffic2, "launch_us": round(sec["launch_us"], 2)}}
+
+    traffic = measured_traffic(args.workload)
+    line = {
+        "metric": METRIC,
+        "value": round(head["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/K/V, per-channel K/V magnitudes U[0.5,2], shuffled block pool)",
+        "config": head["config"],
+        "seq_steps_per_s": round(head["seq_steps_per_s"], 1),
+        "pct_of_hbm_peak": round(head["pct_of_hbm_peak"], 2),
+        "roofline": {"bound": "hbm", "achieved": round(head["achieved"], 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(head["achieved"] / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "launch_us": round(head["launch_us"], 3),
+                     "bytes_per_launch": head["launch_bytes"]},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

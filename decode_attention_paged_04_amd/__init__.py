@@ -55,6 +55,8 @@ EXPORTS = {
     "kvd_decode_workspace_bytes": (ctypes.c_void_p, ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)),
     "kvd_decode_attn": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs), ctypes.c_void_p),
     "kvd_decode_attn_fp8": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs), ctypes.c_void_p),
+    "kvd_decode_partials": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs), ctypes.c_void_p,
+                            ctypes.c_void_p, ctypes.c_void_p),
     "kvd_merge_partials": (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p),
     "kvd_status_string": (ctypes.c_int,),
@@ -143,7 +145,12 @@ def allocate_pool(num_layers: int, num_blocks: int, n_kv: int, head_dim: int,
 
 def kvd_write_kv(pool: Pool, layer: int, k, v, slot_mapping, stream=None):
     """Store bf16 ``k``/``v`` ``[n_tok][n_kv][head_dim]`` at ``slot_mapping`` (int32)."""
+    import torch
     n = int(slot_mapping.numel())
+    shape = (n, pool.desc.n_kv, pool.desc.head_dim)
+    _check_tensor(slot_mapping, "slot_mapping", (n,), torch.int32)
+    _check_tensor(k, "k", shape, torch.bfloat16, slot_mapping.device)
+    _check_tensor(v, "v", shape, torch.bfloat16, slot_mapping.device)
     _check(lib.kvd_write_kv(pool.handle, layer, _ptr(k), _ptr(v), _ptr(slot_mapping), n, _stream(stream)),
            "kvd_write_kv")
 
@@ -157,6 +164,8 @@ def slot_mapping_for(block_table, context_lens):
     import torch
     bt = block_table.to(torch.int64)
     lens = context_lens.to(torch.int64).cpu().tolist()
+    _require(len(lens) == bt.shape[0], "one context length per block-table row")
+    _require(all(0 <= s <= BLOCK_SIZE * bt.shape[1] for s in lens), "context longer than its block-table row")
     parts = []
     for i, s in enumerate(lens):
         t = torch.arange(s, device=bt.device)
@@ -166,12 +175,55 @@ def slot_mapping_for(block_table, context_lens):
     return torch.cat(parts).to(torch.int32)
 
 
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensor(t, name: str, shape, dtype, device=None):
+    import torch
+    _require(t is not None, f"{name} is required")
+    _require(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    _require(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+    _require(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None:
+        _require(t.device == device, f"{name} must be on {device}, got {t.device}")
+
+
 def make_args(q, block_table, context_lens, max_context_len: int, out, lse_out=None,
               chunk_tokens: int = 0, workspace=None, score=None, score_weight: float = 0.0,
-              n_q: Optional[int] = None) -> DecodeArgs:
-    b = int(block_table.shape[0])
+              pool: Optional["Pool"] = None, need_out: bool = True) -> DecodeArgs:
+    """Check every tensor against the others (and the pool) and pack the C struct.
+
+    The C library sees raw pointers only, so this is where sizes are enforced:
+    q ``[b][n_q][d]`` bf16, block_table ``[b][max_blocks]`` int32, context_lens
+    ``[b]`` int32, out like q, lse_out ``[b][n_q]`` fp32, score ``[b][stride]`` fp32,
+    all contiguous and on q's device.
+    """
+    import torch
+    _require(q is not None and q.dim() == 3, "q must be [b][n_q][head_dim]")
+    b, n_q, d = (int(x) for x in q.shape)
+    dev = q.device
+    _check_tensor(q, "q", (b, n_q, d), torch.bfloat16)
+    _require(block_table is not None and block_table.dim() == 2, "block_table must be [b][max_blocks]")
+    _check_tensor(block_table, "block_table", (b, int(block_table.shape[1])), torch.int32, dev)
+    _check_tensor(context_lens, "context_lens", (b,), torch.int32, dev)
+    if need_out or out is not None:
+        _check_tensor(out, "out", (b, n_q, d), torch.bfloat16, dev)
+    if lse_out is not None:
+        _check_tensor(lse_out, "lse_out", (b, n_q), torch.float32, dev)
+    if score is not None:
+        _require(score.dim() == 2, "score must be [b][stride]")
+        _check_tensor(score, "score", (b, int(score.shape[1])), torch.float32, dev)
+    if workspace is not None:
+        _require(workspace.is_contiguous() and workspace.device == dev, "workspace must be contiguous on q's device")
+    if pool is not None:
+        _require(d == pool.desc.head_dim, f"q head_dim {d} != pool head_dim {pool.desc.head_dim}")
+        _require(pool.kv.device == dev, "pool and q must share a device")
+    _require(dev.type == "cuda", "tensors must be on a GPU")
     return DecodeArgs(
-        b, int(n_q if n_q is not None else q.shape[1]), int(block_table.shape[1]), int(max_context_len),
+        b, n_q, int(block_table.shape[1]), int(max_context_len),
         _ptr(q), _ptr(block_table), _ptr(context_lens), _ptr(out), _ptr(lse_out), int(chunk_tokens),
         _ptr(workspace), int(workspace.numel() * workspace.element_size()) if workspace is not None else 0,
         _ptr(score), int(score.shape[1]) if score is not None else 0, float(score_weight))
@@ -209,9 +261,37 @@ def kvd_decode_attn_fp8(pool: Pool, layer: int, args: DecodeArgs, stream=None):
            "kvd_decode_attn_fp8")
 
 
+def kvd_decode_partials(pool: Pool, layer: int, q, block_table, context_lens, max_context_len: int,
+                        part_o=None, part_lse=None, chunk_tokens: int = 0, stream=None):
+    """Per-chunk partials (fp32 o_c ``[b][n_q][n_chunks][d]``, lse_c ``[b][n_q][n_chunks]``).
+
+    Allocates the partial buffers when not given; returns ``(part_o, part_lse, chunk, n_chunks)``.
+    """
+    import torch
+    b, n_q, d = (int(x) for x in q.shape)
+    args = make_args(q, block_table, context_lens, max_context_len, None, chunk_tokens=chunk_tokens,
+                     pool=pool, need_out=False)
+    chunk, nc = kvd_decode_plan(pool, args)
+    if part_o is None:
+        part_o = torch.empty((b, n_q, nc, d), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((b, n_q, nc), dtype=torch.float32, device=q.device)
+    _check_tensor(part_o, "part_o", (b, n_q, nc, d), torch.float32, q.device)
+    _check_tensor(part_lse, "part_lse", (b, n_q, nc), torch.float32, q.device)
+    _check(lib.kvd_decode_partials(pool.handle, layer, ctypes.byref(args), _ptr(part_o), _ptr(part_lse),
+                                   _stream(stream)), "kvd_decode_partials")
+    return part_o, part_lse, chunk, nc
+
+
 def kvd_merge_partials(part_o, part_lse, out, lse_out=None, stream=None):
     """part_o fp32 ``[b][n_q][n_chunks][d]``, part_lse ``[b][n_q][n_chunks]`` -> out bf16."""
+    import torch
     b, n_q, nc, d = (int(x) for x in part_o.shape)
+    _check_tensor(part_o, "part_o", (b, n_q, nc, d), torch.float32)
+    _check_tensor(part_lse, "part_lse", (b, n_q, nc), torch.float32, part_o.device)
+    _check_tensor(out, "out", (b, n_q, d), torch.bfloat16, part_o.device)
+    if lse_out is not None:
+        _check_tensor(lse_out, "lse_out", (b, n_q), torch.float32, part_o.device)
     _check(lib.kvd_merge_partials(_ptr(part_o), _ptr(part_lse), b, n_q, nc, d, _ptr(out), _ptr(lse_out),
                                   _stream(stream)), "kvd_merge_partials")
 
@@ -221,12 +301,19 @@ def kvd_status_string(status: int) -> str:
 
 
 def kvd_debug_gather_offsets(pool: Pool, layer: int, block_table, n_tok: int, out_k, out_v, stream=None):
+    import torch
     b, mb = (int(x) for x in block_table.shape)
+    _check_tensor(block_table, "block_table", (b, mb), torch.int32)
+    _check_tensor(out_k, "out_k", (b, pool.desc.n_kv, n_tok), torch.int64, block_table.device)
+    _check_tensor(out_v, "out_v", (b, pool.desc.n_kv, n_tok), torch.int64, block_table.device)
     _check(lib.kvd_debug_gather_offsets(pool.handle, layer, _ptr(block_table), mb, b, n_tok, _ptr(out_k),
                                         _ptr(out_v), _stream(stream)), "kvd_debug_gather_offsets")
 
 
 def kvd_debug_fp8_decode(codes, out, stream=None):
+    import torch
+    _check_tensor(codes, "codes", (int(codes.numel()),), torch.uint8)
+    _check_tensor(out, "out", (int(codes.numel()),), torch.float32, codes.device)
     _check(lib.kvd_debug_fp8_decode(_ptr(codes), int(codes.numel()), _ptr(out), _stream(stream)),
            "kvd_debug_fp8_decode")
 
@@ -239,7 +326,7 @@ def decode(pool: Pool, layer: int, q, block_table, context_lens, max_context_len
     if out is None:
         out = torch.empty_like(q)
     args = make_args(q, block_table, context_lens, max_context_len, out, lse_out, chunk_tokens,
-                     workspace, score, score_weight)
+                     workspace, score, score_weight, pool=pool)
     ws = workspace
     if ws is None:
         ws = allocate_workspace(pool, args, device=q.device)

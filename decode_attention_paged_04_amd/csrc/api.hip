@@ -21,6 +21,11 @@ constexpr int32_t kChunkQuantum = 128;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Launch status is read back with hipGetLastError, which also reports an error
+// left behind by an earlier, unrelated runtime call in this thread; clear that
+// first so that only this call's launches are judged.
+void clear_stale_error() { (void)hipGetLastError(); }
+
 kvd_status check_desc(const kvd_pool_desc* d) {
   if (!d) return KVD_ERR_INVALID_ARG;
   if (d->num_layers < 1 || d->num_blocks < 1 || d->n_kv < 1) return KVD_ERR_INVALID_ARG;
@@ -80,22 +85,31 @@ kvd_status plan_decode(const PoolView& p, const kvd_decode_args* a, DecodePlan* 
   return KVD_OK;
 }
 
+// One decode call.  ext_part_o / ext_part_lse (both or neither): write the
+// per-chunk partials there and stop, instead of producing the merged output.
 kvd_status decode_common(const kvd_pool* pool, int32_t layer, const kvd_decode_args* a,
-                         void* stream, kvd_dtype want) {
+                         void* stream, bool any_dtype, kvd_dtype want, float* ext_part_o,
+                         float* ext_part_lse) {
   if (!pool || !a) return KVD_ERR_INVALID_ARG;
   const PoolView& p = pool->v;
-  if (p.dtype != want) return KVD_ERR_DTYPE;
+  if (!any_dtype && p.dtype != want) return KVD_ERR_DTYPE;
   if (layer < 0 || layer >= p.num_layers) return KVD_ERR_INVALID_ARG;
+  const bool external = ext_part_o != nullptr || ext_part_lse != nullptr;
+  if (external && (a->score || !ext_part_o || !ext_part_lse)) return KVD_ERR_INVALID_ARG;
   DecodePlan pl;
   kvd_status st = plan_decode(p, a, &pl);
   if (st != KVD_OK) return st;
   if (a->b == 0) return KVD_OK;
-  if (!a->q || !a->block_table || !a->context_lens || !a->out) return KVD_ERR_INVALID_ARG;
-  if (pl.total > 0) {
+  if (!a->q || !a->block_table || !a->context_lens) return KVD_ERR_INVALID_ARG;
+  if (!external && !a->out) return KVD_ERR_INVALID_ARG;
+  if (!external && pl.total > 0) {
     if (!a->workspace || a->workspace_bytes < pl.total) return KVD_ERR_WORKSPACE;
     if (((uintptr_t)a->workspace & 255) != 0) return KVD_ERR_WORKSPACE;
   }
+  if (external && ((((uintptr_t)ext_part_o) & 15) != 0 || (((uintptr_t)ext_part_lse) & 3) != 0))
+    return KVD_ERR_INVALID_ARG;
   char* ws = static_cast<char*>(a->workspace);
+  const bool final_direct = !external && pl.final_direct;
   kvd::DecodeLaunch L{};
   L.layer_base = p.kv_base + (size_t)layer * (size_t)p.layer_bytes;
   L.layer_bytes = (uint32_t)p.layer_bytes;
@@ -114,20 +128,28 @@ kvd_status decode_common(const kvd_pool* pool, int32_t layer, const kvd_decode_a
   L.n_chunks = pl.n_chunks;
   L.out = static_cast<uint16_t*>(a->out);
   L.lse_out = a->lse_out;
-  L.part_o = pl.final_direct ? nullptr : reinterpret_cast<float*>(ws + pl.off_part_o);
-  L.part_lse = pl.final_direct ? nullptr : reinterpret_cast<float*>(ws + pl.off_part_lse);
-  L.logits = pl.scores ? reinterpret_cast<float*>(ws + pl.off_logits) : nullptr;
-  L.lse2 = pl.scores ? reinterpret_cast<float*>(ws + pl.off_lse2) : nullptr;
+  if (external) {
+    L.part_o = ext_part_o;
+    L.part_lse = ext_part_lse;
+  } else if (!final_direct) {
+    L.part_o = reinterpret_cast<float*>(ws + pl.off_part_o);
+    L.part_lse = reinterpret_cast<float*>(ws + pl.off_part_lse);
+  }
+  const bool scores = !external && pl.scores;
+  L.logits = scores ? reinterpret_cast<float*>(ws + pl.off_logits) : nullptr;
+  L.lse2 = scores ? reinterpret_cast<float*>(ws + pl.off_lse2) : nullptr;
   L.logit_stride = pl.logit_stride;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (kvd::launch_decode(L, p.head_dim, want == KVD_FP8_E4M3, pl.final_direct, pl.scores, s) != hipSuccess)
+  clear_stale_error();
+  if (kvd::launch_decode(L, p.head_dim, p.dtype == KVD_FP8_E4M3, final_direct, scores, s) != hipSuccess)
     return KVD_ERR_HIP;
-  if (!pl.final_direct) {
+  if (external) return KVD_OK;
+  if (!final_direct) {
     if (kvd::launch_merge(L.part_o, L.part_lse, a->context_lens, pl.ctx_bound, pl.chunk, a->b,
                           a->n_q, pl.n_chunks, p.head_dim, L.out, a->lse_out, L.lse2, s) != hipSuccess)
       return KVD_ERR_HIP;
   }
-  if (pl.scores) {
+  if (scores) {
     if (kvd::launch_score(L.logits, L.lse2, a->context_lens, pl.ctx_bound, a->b, a->n_q,
                           pl.logit_stride, a->score, a->score_stride, a->score_weight, s) != hipSuccess)
       return KVD_ERR_HIP;
@@ -189,6 +211,7 @@ kvd_status kvd_write_kv(const kvd_pool* pool, int32_t layer, const void* k, cons
   if (n_tok == 0) return KVD_OK;
   if (!k || !v || !slot_mapping) return KVD_ERR_INVALID_ARG;
   if ((int64_t)n_tok * pool->v.n_kv * pool->v.head_dim >= ((int64_t)1 << 40)) return KVD_ERR_UNSUPPORTED;
+  clear_stale_error();
   if (kvd::launch_write(pool->v, layer, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                         slot_mapping, n_tok, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
     return KVD_ERR_HIP;
@@ -216,12 +239,18 @@ kvd_status kvd_decode_workspace_bytes(const kvd_pool* pool, const kvd_decode_arg
 }
 
 kvd_status kvd_decode_attn(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args, void* hip_stream) {
-  return decode_common(pool, layer, args, hip_stream, KVD_BF16);
+  return decode_common(pool, layer, args, hip_stream, false, KVD_BF16, nullptr, nullptr);
 }
 
 kvd_status kvd_decode_attn_fp8(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
                                void* hip_stream) {
-  return decode_common(pool, layer, args, hip_stream, KVD_FP8_E4M3);
+  return decode_common(pool, layer, args, hip_stream, false, KVD_FP8_E4M3, nullptr, nullptr);
+}
+
+kvd_status kvd_decode_partials(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
+                               float* part_o, float* part_lse, void* hip_stream) {
+  if (!part_o || !part_lse) return KVD_ERR_INVALID_ARG;
+  return decode_common(pool, layer, args, hip_stream, true, KVD_BF16, part_o, part_lse);
 }
 
 kvd_status kvd_merge_partials(const float* part_o, const float* part_lse, int32_t b, int32_t n_q,
@@ -232,6 +261,7 @@ kvd_status kvd_merge_partials(const float* part_o, const float* part_lse, int32_
   if (b == 0) return KVD_OK;
   if (!part_o || !part_lse || !out_bf16) return KVD_ERR_INVALID_ARG;
   if ((int64_t)b * n_q >= ((int64_t)1 << 31)) return KVD_ERR_UNSUPPORTED;
+  clear_stale_error();
   if (kvd::launch_merge(part_o, part_lse, nullptr, 0, 1, b, n_q, n_chunks, d_h,
                         static_cast<uint16_t*>(out_bf16), lse_out, nullptr,
                         static_cast<hipStream_t>(hip_stream)) != hipSuccess)
@@ -259,6 +289,7 @@ kvd_status kvd_debug_gather_offsets(const kvd_pool* pool, int32_t layer, const i
   if ((int64_t)n_tok > (int64_t)kvd::kBlock * max_blocks_per_seq) return KVD_ERR_INVALID_ARG;
   if ((int64_t)b * n_tok == 0) return KVD_OK;
   if (!block_table || !out_k || !out_v) return KVD_ERR_INVALID_ARG;
+  clear_stale_error();
   if (kvd::launch_debug_offsets(pool->v, layer, block_table, max_blocks_per_seq, b, n_tok, out_k, out_v,
                                 static_cast<hipStream_t>(hip_stream)) != hipSuccess)
     return KVD_ERR_HIP;
@@ -269,6 +300,7 @@ kvd_status kvd_debug_fp8_decode(const uint8_t* codes, int32_t n, float* out, voi
   if (n < 0) return KVD_ERR_INVALID_ARG;
   if (n == 0) return KVD_OK;
   if (!codes || !out) return KVD_ERR_INVALID_ARG;
+  clear_stale_error();
   if (kvd::launch_debug_fp8_decode(codes, n, out, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
     return KVD_ERR_HIP;
   return KVD_OK;

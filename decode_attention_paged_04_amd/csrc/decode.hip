@@ -6,7 +6,9 @@
 //   * reads the two physical block ids from the block table and streams the
 //     pair's K and V tiles from HBM straight into registers, in the operand
 //     layout of the 16x16x32 bf16 MFMA (16-byte loads through a bounded buffer
-//     resource, so a bad block id reads zeros instead of faulting);
+//     resource, so a bad block id reads zeros instead of faulting).  The loads
+//     of the wave's next pair are issued before the current pair is consumed,
+//     so two pairs (32 KiB for bf16, d_h = 128) are in flight per wave;
 //   * computes S = K q^T for all g query heads of KV head j at once (MFMA rows =
 //     tokens, columns = heads, so each K tile is read once and shared by the g
 //     heads -- the GQA saving);
@@ -16,8 +18,8 @@
 //     so that the product keeps ~16 bits of P (a single bf16 P would add a
 //     relative error of ~1e-3 to the output).
 // The four waves' (max, sum, O) are then combined through LDS and written
-// either as the final bf16 output (single chunk) or as an fp32 partial for
-// the log-sum-exp merge.
+// either as the final bf16 output (single chunk) or as an fp32 partial
+// (o_c normalised, lse_c natural log) for the log-sum-exp merge kernel.
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16 (lane l, G = l / 16, r = l % 16):
 // A[row r][k in group G], B[k in group G][col r], D[row 4G + q][col r], q < 4.
@@ -41,14 +43,17 @@ constexpr int kWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Registers holding one pair's K/V (and, for FP8, its scales) between the
+// loads and their use.
 template <int D, bool FP8>
-struct Pair {
+struct PairRegs {
   static constexpr int E = FP8 ? 1 : 2;        // bytes per element
   static constexpr int KU = D * E / 64;        // 16-byte K units per lane per S-tile
   static constexpr int NM = D / 16;            // 16-channel tiles of the output
   u32x4 k[2][KU];
   u32x4 v[FP8 ? 1 : NM];                       // bf16 V: 16 B per lane per channel tile
   u32x2 v8[FP8 ? NM : 1];                      // FP8 V: 8 B per lane per channel tile
+  float sK, sV;                                // FP8 scales of this lane's block
 };
 
 // k index group G of MFMA step c covers these 8 channels of q and K.
@@ -58,10 +63,10 @@ __device__ inline int qk_channel0(int c, int G) {
 }
 
 template <int D, bool FP8, bool FINAL, bool SCORES>
-__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeLaunch a) {
-  using P = Pair<D, FP8>;
-  constexpr int E = P::E;
-  constexpr int NM = P::NM;
+__global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeLaunch a) {
+  using R = PairRegs<D, FP8>;
+  constexpr int E = R::E;
+  constexpr int NM = R::NM;
   constexpr int NC = D / 32;                   // MFMA steps along the head dim
   constexpr uint32_t TPB = 2u * kBlock * D * E;
 
@@ -79,15 +84,19 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeLaunch a) {
   s = s < 0 ? 0 : (s > a.ctx_bound ? a.ctx_bound : s);
   const int lo = c * a.chunk;
   const int ntok = min(s, lo + a.chunk) - lo;
-  if (!FINAL && ntok <= 0) return;             // empty chunk: the merge skips it
-
   const int g = a.g;
   const bool head_ok = r16 < g;
+  const size_t ih = (size_t)i * a.n_q + (size_t)j * g + r16;   // this lane's head (when head_ok)
+  if (!FINAL && ntok <= 0) {
+    // Chunk past the end of the sequence: it contributes nothing to the merge.
+    if (wave == 0 && G == 0 && head_ok) a.part_lse[ih * a.n_chunks + c] = -INFINITY;
+    return;
+  }
 
   // q as the B operand of S = K q^T: column r16 = query head j*g + r16.
   bf16x8 qf[NC];
   {
-    const uint16_t* qrow = a.q + ((size_t)i * a.n_q + (size_t)j * g + r16) * D;
+    const uint16_t* qrow = a.q + ih * D;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       u32x4 raw = {0u, 0u, 0u, 0u};
@@ -107,41 +116,40 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeLaunch a) {
   for (int mm = 0; mm < NM; ++mm) o[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int npairs = (ntok + 31) >> 5;
-  for (int p = wave; p < npairs; p += kWaves) {
-    const int tok0 = p << 5;
-    const int nvalid = min(32, ntok - tok0);
-    const int32_t pid0 = bt[2 * p];
-    const int32_t pid1 = nvalid > kBlock ? bt[2 * p + 1] : -1;
+
+  // Issue every load of pair p into f.  A pair past the end (p >= npairs)
+  // issues the same loads at out-of-range offsets: they return zeros without
+  // touching memory, and the number of loads in flight stays the same on every
+  // path, so the waits before each use cover exactly the pair being used.
+  auto issue = [&](R& f, int p) {
+    const bool live = p < npairs;
+    const int nvalid = min(32, ntok - (p << 5));
+    const int32_t pid0 = live ? bt[2 * p] : -1;
+    const int32_t pid1 = live && nvalid > kBlock ? bt[2 * p + 1] : -1;
     const uint32_t t0 = tile_pair_offset(pid0, j, a.num_blocks, a.n_kv, TPB);
     const uint32_t t1 = tile_pair_offset(pid1, j, a.num_blocks, a.n_kv, TPB);
-
-    P d;
-    {
-      // K: S-tile t, row r16 -> block r16/8, in-block row 8*((r16/4)&1) + 4t + r16%4;
-      // this lane's 16-byte units sit at byte 64u + 16G of that row.
-      const uint32_t tk = r16 < 8 ? t0 : t1;
+    // K: S-tile t, row r16 -> block r16/8, in-block row 8*((r16/4)&1) + 4t + r16%4;
+    // this lane's 16-byte units sit at byte 64u + 16G of that row.
+    const uint32_t tk = r16 < 8 ? t0 : t1;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int row = 8 * ((r16 >> 2) & 1) + 4 * t + (r16 & 3);
+    for (int t = 0; t < 2; ++t) {
+      const int row = 8 * ((r16 >> 2) & 1) + 4 * t + (r16 & 3);
 #pragma unroll
-        for (int u = 0; u < P::KU; ++u) {
-          const uint32_t off = tk + (uint32_t)(row * D * E + 64 * u + 16 * G);
-          d.k[t][u] = load16(rs, tk == kOutOfRange ? kOutOfRange : off);
-        }
-      }
-      // V (channel-major): channel tile mm, channel 16mm + r16, rows 8(G&1) .. +7
-      // of block G/2.
-      const uint32_t tv = G < 2 ? t0 : t1;
-#pragma unroll
-      for (int mm = 0; mm < NM; ++mm) {
-        const uint32_t off = tv + (uint32_t)((v_elem(8 * (G & 1), 16 * mm + r16, D)) * E);
-        const uint32_t o2 = tv == kOutOfRange ? kOutOfRange : off;
-        if constexpr (FP8) d.v8[mm] = load8(rs, o2);
-        else d.v[mm] = load16(rs, o2);
+      for (int u = 0; u < R::KU; ++u) {
+        const uint32_t off = tk + (uint32_t)(row * D * E + 64 * u + 16 * G);
+        f.k[t][u] = load16(rs, tk == kOutOfRange ? kOutOfRange : off);
       }
     }
-
-    float sK = 1.f, sV = 1.f;
+    // V (channel-major): channel tile mm, channel 16mm + r16, rows 8(G&1) .. +7
+    // of block G/2.
+    const uint32_t tv = G < 2 ? t0 : t1;
+#pragma unroll
+    for (int mm = 0; mm < NM; ++mm) {
+      const uint32_t off = tv + (uint32_t)((v_elem(8 * (G & 1), 16 * mm + r16, D)) * E);
+      const uint32_t o2 = tv == kOutOfRange ? kOutOfRange : off;
+      if constexpr (FP8) f.v8[mm] = load8(rs, o2);
+      else f.v[mm] = load16(rs, o2);
+    }
     if constexpr (FP8) {
       // fp32 scales of this lane's block (G/2) for K and V; zero for a bad id.
       const float* sc = a.layer_scales;
@@ -149,11 +157,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeLaunch a) {
       const float sv0 = t0 == kOutOfRange ? 0.f : sc[((size_t)pid0 * a.n_kv + j) * 2 + 1];
       const float sk1 = t1 == kOutOfRange ? 0.f : sc[((size_t)pid1 * a.n_kv + j) * 2 + 0];
       const float sv1 = t1 == kOutOfRange ? 0.f : sc[((size_t)pid1 * a.n_kv + j) * 2 + 1];
-      sK = G < 2 ? sk0 : sk1;
-      sV = G < 2 ? sv0 : sv1;
+      f.sK = G < 2 ? sk0 : sk1;
+      f.sV = G < 2 ? sv0 : sv1;
     }
+  };
 
-    // S = K q^T for both S-tiles.
+  // Fold pair p (held in f) into the running state.
+  auto consume = [&](R& f, int p) {
+    const int tok0 = p << 5;
+    const int nvalid = min(32, ntok - tok0);
+
     f32x4 sacc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -162,10 +175,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeLaunch a) {
       for (int cc = 0; cc < NC; ++cc) {
         bf16x8 kf;
         if constexpr (FP8) {
-          const u32x4 w = d.k[t][cc >> 1];
+          const u32x4 w = f.k[t][cc >> 1];
           kf = (cc & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
         } else {
-          kf = __builtin_bit_cast(bf16x8, d.k[t][cc]);
+          kf = __builtin_bit_cast(bf16x8, f.k[t][cc]);
         }
         sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[cc], sacc[t], 0, 0, 0);
       }
@@ -173,7 +186,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeLaunch a) {
 
     // Scaled scores; lane element e = 4t + q is pair token 8G + e.
     float xs[8];
-    const float sc_all = qk_scale * sK;
+    const float sc_all = FP8 ? qk_scale * f.sK : qk_scale;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -188,8 +201,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeLaunch a) {
 
     if constexpr (SCORES) {
       if (head_ok) {
-        float* dst = a.logits + ((size_t)i * a.n_q + (size_t)j * g + r16) * a.logit_stride +
-                     lo + tok0 + 8 * G;
+        float* dst = a.logits + ih * a.logit_stride + lo + tok0 + 8 * G;
         *reinterpret_cast<f32x4*>(dst) = f32x4{xs[0], xs[1], xs[2], xs[3]};
         *reinterpret_cast<f32x4*>(dst + 4) = f32x4{xs[4], xs[5], xs[6], xs[7]};
       }
@@ -219,7 +231,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeLaunch a) {
     bf16x8 phi, plo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = pv[e] * sV;
+      const float pe = FP8 ? pv[e] * f.sV : pv[e];
       const __bf16 h = (__bf16)pe;
       phi[e] = h;
       plo[e] = (__bf16)(pe - (float)h);
@@ -239,8 +251,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeLaunch a) {
         }
 #pragma unroll
         for (int mm = 0; mm < NM; ++mm) {
-          d.v8[mm][0] &= keep[0];
-          d.v8[mm][1] &= keep[1];
+          f.v8[mm][0] &= keep[0];
+          f.v8[mm][1] &= keep[1];
         }
       } else {
         uint32_t keep[4];
@@ -250,7 +262,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeLaunch a) {
 #pragma unroll
         for (int mm = 0; mm < NM; ++mm)
 #pragma unroll
-          for (int w = 0; w < 4; ++w) d.v[mm][w] &= keep[w];
+          for (int w = 0; w < 4; ++w) f.v[mm][w] &= keep[w];
       }
     }
 
@@ -258,11 +270,31 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeLaunch a) {
 #pragma unroll
     for (int mm = 0; mm < NM; ++mm) {
       bf16x8 vf;
-      if constexpr (FP8) vf = e4m3x8_to_bf16x8(d.v8[mm][0], d.v8[mm][1]);
-      else vf = __builtin_bit_cast(bf16x8, d.v[mm]);
+      if constexpr (FP8) vf = e4m3x8_to_bf16x8(f.v8[mm][0], f.v8[mm][1]);
+      else vf = __builtin_bit_cast(bf16x8, f.v[mm]);
       o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi, o[mm], 0, 0, 0);
       o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo, o[mm], 0, 0, 0);
     }
+  };
+
+  // Two register sets: the next pair's loads are in flight while the current
+  // pair is consumed.  This wave owns pairs wave, wave + kWaves, ...; they are
+  // taken two at a time so that every pass through the loop has the same
+  // loads outstanding (a load past the end is an out-of-range no-op).
+  const int nmine = npairs > wave ? (npairs - wave + kWaves - 1) / kWaves : 0;
+  if (nmine > 0) {
+    R fa, fb;
+    int p = wave;
+    issue(fa, p);
+    int k = 0;
+    for (; k + 1 < nmine; k += 2) {
+      issue(fb, p + kWaves);
+      consume(fa, p);
+      issue(fa, p + 2 * kWaves);
+      consume(fb, p + kWaves);
+      p += 2 * kWaves;
+    }
+    if (k < nmine) consume(fa, p);
   }
 
   // Whole-head sum of this wave.
@@ -294,7 +326,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeLaunch a) {
   const bool empty = !(L > 0.f);
   const float inv_l = empty ? 0.f : 1.0f / L;
   const float lse2 = empty ? -INFINITY : M + __log2f(L);
-  const size_t ih = (size_t)i * a.n_q + (size_t)j * g + r16;   // valid when head_ok
   for (int mm = wave; mm < NM; mm += kWaves) {
     f32x4 acc = sh_o[0][mm][lane];
 #pragma unroll

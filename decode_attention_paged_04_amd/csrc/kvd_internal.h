@@ -27,7 +27,7 @@ struct DecodePlan {
   int32_t n_chunks;         // chunks per sequence at max_context_len
   int32_t ctx_bound;        // clamp for every s_i
   int32_t logit_stride;     // row length of the logit scratch (scores only)
-  bool final_direct;        // one chunk: the decode kernel writes out/lse itself
+  bool final_direct;        // one chunk: no partials, the workgroup writes out/lse itself
   bool scores;
   size_t off_part_o, off_part_lse, off_logits, off_lse2, total;
 };

@@ -1,5 +1,5 @@
-// Log-sum-exp merge of per-chunk partials, and the fused cumulative-score
-// update that needs the merged lse.
+// Log-sum-exp merge of per-chunk partials, and the cumulative-score update
+// that needs the merged lse.
 #include "device_common.h"
 #include "kvd_internal.h"
 
@@ -7,51 +7,84 @@
 
 namespace kvd {
 
-constexpr float kLog2eM = 1.4426950408889634f;
+constexpr float kLog2eMerge = 1.4426950408889634f;
+constexpr int kMergeThreads = 256;
 
-// One workgroup per (sequence, query head); thread t owns channel t.
-// lse = M + ln(sum_c exp(lse_c - M)), out = sum_c exp(lse_c - lse) * o_c.
+template <bool MAX>
+__device__ inline float block_reduce(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float o = __shfl_xor(v, off);
+    v = MAX ? fmaxf(v, o) : v + o;
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();                               // red may still be read by a previous call
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  v = red[0];
+#pragma unroll
+  for (int k = 1; k < kMergeThreads / 64; ++k) v = MAX ? fmaxf(v, red[k]) : v + red[k];
+  return v;
+}
+
+// One workgroup per (sequence, query head).  lse = M + ln(sum_c exp(lse_c - M))
+// with M = max_c lse_c over the first nc chunks; out = sum_c exp(lse_c - lse) *
+// o_c, rounded to bf16.  A chunk whose weight is 0 (lse_c = -inf) is never
+// read, so its o_c may hold anything.  No chunk, or only empty ones: out = 0,
+// lse = -inf.  The thread count splits the chunks into 256 / D interleaved
+// groups, one channel per thread, summed at the end in a fixed order.
 template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(const float* __restrict__ part_o,
-                                                  const float* __restrict__ part_lse,
-                                                  const int32_t* __restrict__ context_lens,
-                                                  int32_t ctx_bound, int32_t chunk, int32_t n_q,
-                                                  int32_t n_chunks, uint16_t* __restrict__ out,
-                                                  float* __restrict__ lse_out,
-                                                  float* __restrict__ lse2) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse,
+    const int32_t* __restrict__ context_lens, int32_t ctx_bound, int32_t chunk, int32_t n_q,
+    int32_t n_chunks, uint16_t* __restrict__ out, float* __restrict__ lse_out,
+    float* __restrict__ lse2) {
+  constexpr int NG = kMergeThreads / D;
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ float acc_s[kMergeThreads];
   const size_t ih = blockIdx.x;
-  const int i = (int)(ih / n_q);
   int nc = n_chunks;
   if (context_lens) {
-    int s = context_lens[i];
+    int s = context_lens[ih / n_q];
     s = s < 0 ? 0 : (s > ctx_bound ? ctx_bound : s);
     nc = min(n_chunks, (s + chunk - 1) / chunk);
   }
   const float* pl = part_lse + ih * n_chunks;
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, pl[c]);
+  const float* po = part_o + ih * n_chunks * D;
   const int t = threadIdx.x;
+
+  float mx = -INFINITY;
+  for (int c = t; c < nc; c += kMergeThreads) mx = fmaxf(mx, pl[c]);
+  const float M = block_reduce<true>(mx, red);
+  const int ch = t % D, grp = t / D;
   if (M == -INFINITY) {
-    out[ih * D + t] = 0;
+    if (grp == 0) out[ih * D + ch] = 0;
     if (t == 0) {
       if (lse_out) lse_out[ih] = -INFINITY;
       if (lse2) lse2[ih] = -INFINITY;
     }
     return;
   }
-  float L = 0.f;
-  for (int c = 0; c < nc; ++c) L += expf(pl[c] - M);
-  const float lse = M + logf(L);
-  const float* po = part_o + ih * n_chunks * D + t;
+  float sm = 0.f;
+  for (int c = t; c < nc; c += kMergeThreads) sm += expf(pl[c] - M);
+  const float lse = M + logf(block_reduce<false>(sm, red));
+
   float acc = 0.f;
-  for (int c = 0; c < nc; ++c) {
+#pragma unroll 8
+  for (int c = grp; c < nc; c += NG) {
     const float w = expf(pl[c] - lse);
-    if (w != 0.f) acc += w * po[(size_t)c * D];
+    if (w != 0.f) acc += w * po[(size_t)c * D + ch];
   }
-  out[ih * D + t] = float_to_bf16_bits(acc);
+  acc_s[t] = acc;
+  __syncthreads();
+  if (grp == 0) {
+#pragma unroll
+    for (int k = 1; k < NG; ++k) acc += acc_s[k * D + ch];
+    out[ih * D + ch] = float_to_bf16_bits(acc);
+  }
   if (t == 0) {
     if (lse_out) lse_out[ih] = lse;
-    if (lse2) lse2[ih] = lse * kLog2eM;
+    if (lse2) lse2[ih] = lse * kLog2eMerge;
   }
 }
 
@@ -81,10 +114,10 @@ hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_
                         float* lse2, hipStream_t stream) {
   const dim3 grid((unsigned)((size_t)b * n_q));
   if (head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(128), 0, stream, part_o, part_lse,
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, part_o, part_lse,
                        context_lens, ctx_bound, chunk, n_q, n_chunks, out, lse_out, lse2);
   else
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, stream, part_o, part_lse,
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, stream, part_o, part_lse,
                        context_lens, ctx_bound, chunk, n_q, n_chunks, out, lse_out, lse2);
   return hipGetLastError();
 }

@@ -132,7 +132,8 @@ typedef struct {
                               /* log-sum-exp of the scaled scores (-inf if s_i = 0)   */
   int32_t chunk_tokens;       /* context split: 0 = automatic, else a multiple of 16  */
   void* workspace;            /* device scratch of kvd_decode_workspace_bytes bytes,  */
-  size_t workspace_bytes;     /* 256-byte aligned; may be NULL when that size is 0    */
+  size_t workspace_bytes;     /* 256-byte aligned; may be NULL when that size is 0.   */
+                              /* Calls that overlap in time must not share one.       */
   float* score;               /* optional device fp32 [b][score_stride] cumulative    */
   int32_t score_stride;       /* score; >= max_context_len when score is set          */
   float score_weight;         /* score[i][t] += score_weight * mean_h alpha_h(t)      */
@@ -144,15 +145,20 @@ kvd_status kvd_decode_plan(const kvd_pool* pool, const kvd_decode_args* args,
                            int32_t* chunk_tokens, int32_t* n_chunks);
 
 /* Workspace bytes a decode call with these arguments needs (0 when the whole
- * context fits one chunk and no score is requested).  Pure host function. */
+ * context fits one chunk and no score is requested): the per-chunk partials
+ * and, with a score, the scaled scores and lse of the call.  Pure host
+ * function. */
 kvd_status kvd_decode_workspace_bytes(const kvd_pool* pool, const kvd_decode_args* args,
                                       size_t* bytes);
 
 /* One decode-attention step of one layer on a bf16 pool.
  * Each (sequence, KV head, context chunk) is processed by one workgroup that
  * streams the chunk's K/V blocks once and serves all g query heads of the KV
- * head from them.  With more than one chunk the per-chunk results are merged
- * by log-sum-exp (kvd_merge_partials' arithmetic) inside the same call.
+ * head from them.  With one chunk that workgroup writes the output; with
+ * more, a second kernel merges the per-chunk results by log-sum-exp
+ * (kvd_merge_partials' arithmetic, restricted to each sequence's chunks).
+ * With score a further kernel adds the weights once every head's lse is
+ * known.
  * With score set, adds score_weight * (1/n_q) * sum_h alpha_h(t) to
  * score[i][t] for every t < s_i, alpha_h(t) being the softmax weight of
  * token t for head h -- the per-layer term of the cumulative attention score
@@ -170,10 +176,25 @@ kvd_status kvd_decode_attn(const kvd_pool* pool, int32_t layer, const kvd_decode
 kvd_status kvd_decode_attn_fp8(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
                                void* hip_stream);
 
+/* Per-chunk partial results of one decode step of one layer, for a caller
+ * that merges them itself -- for example the partials of context shards held
+ * by several GPUs, combined with kvd_merge_partials.  Works on bf16 and FP8
+ * pools alike.  The context is split as kvd_decode_plan reports: n_chunks
+ * chunks of chunk_tokens tokens, chunk c covering tokens [c*chunk, (c+1)*chunk)
+ * of each sequence, always as partials (also when n_chunks is 1).
+ * part_o:   device fp32 [b][n_q][n_chunks][d_h], 16-byte aligned: each chunk's
+ *           own normalised output;
+ * part_lse: device fp32 [b][n_q][n_chunks]: natural-log lse of the chunk's
+ *           scaled scores, -inf for a chunk past the end of its sequence (whose
+ *           part_o row is left unwritten).
+ * args->out, lse_out and workspace are not used; args->score must be NULL. */
+kvd_status kvd_decode_partials(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
+                               float* part_o, float* part_lse, void* hip_stream);
+
 /* Merge per-chunk partial results by log-sum-exp.
  * part_o:   device fp32 [b][n_q][n_chunks][d_h], each chunk's normalised output
  * part_lse: device fp32 [b][n_q][n_chunks], natural log; -inf marks an empty
- *           chunk, which contributes nothing
+ *           chunk, which contributes nothing (its part_o row is never read)
  * out_bf16: device bf16 [b][n_q][d_h]; lse_out: optional fp32 [b][n_q].
  * lse = M + ln(sum_c exp(lse_c - M)), M = max_c lse_c, and
  * out = sum_c exp(lse_c - lse) * o_c, rounded to bf16 (nearest even).

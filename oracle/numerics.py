@@ -46,3 +46,10 @@ def f64_to_bf16_bits(x) -> np.ndarray:
 def round_to_bf16(x) -> np.ndarray:
     """float64 values rounded to bf16 (nearest-even), returned as float64."""
     return bf16_bits_to_f64(f64_to_bf16_bits(x))
+
+
+def bf16_ulp(x) -> np.ndarray:
+    """Spacing of bf16 numbers at |x|: 2^(e-7) for |x| in [2^e, 2^(e+1)), at least 2^-133."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(np.where(a > 0, a, 1.0))
+    return np.ldexp(1.0, np.maximum(e - 1 - 7, -133))

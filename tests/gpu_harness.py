@@ -16,9 +16,13 @@ from oracle import attention, e4m3, numerics, paged, scores
 DEV = "cuda"
 
 # Tolerances.  bf16 outputs are compared with the oracle rounded to bf16
-# (nearest even): max-abs 4e-3 and relative L2 1e-3 per output tensor of one
-# layer call.  FP8 pools: relative L2 1e-2 against the oracle run on the same
-# E4M3 codes.  Cumulative scores: 1e-5 relative per element.
+# (nearest even): relative L2 1e-3 per output tensor of one layer call, and per
+# element an absolute error of at most 4e-3 -- or of one bf16 spacing at the
+# reference value, which is what a single rounding-boundary flip costs when the
+# output's magnitude is 1 or more (the spacing there is 2^-7 or wider, so no
+# bf16 result could meet 4e-3 on its own).  FP8 pools: relative L2 1e-2
+# against the oracle run on the same E4M3 codes.  Cumulative scores: 1e-5
+# relative per element.
 TOL_MAX_ABS = 4e-3
 TOL_REL_L2 = 1e-3
 TOL_FP8_REL_L2 = 1e-2
@@ -35,18 +39,22 @@ def bf16_to_f64(t) -> np.ndarray:
 
 
 def bf16_errors(got, ref_f64: np.ndarray):
-    """(max-abs, rel-L2) of bf16 ``got`` against the oracle rounded to bf16."""
+    """(max-abs, rel-L2, worst element error over its allowance) of bf16 ``got``
+    against the oracle rounded to bf16."""
     g = bf16_to_f64(got)
     r = numerics.round_to_bf16(ref_f64)
-    err = g - r
+    err = np.abs(g - r)
     denom = np.linalg.norm(r)
     rel = float(np.linalg.norm(err) / denom) if denom > 0 else float(np.linalg.norm(err))
-    return float(np.max(np.abs(err))) if err.size else 0.0, rel
+    if not err.size:
+        return 0.0, rel, 0.0
+    allow = np.maximum(TOL_MAX_ABS, numerics.bf16_ulp(r))
+    return float(np.max(err)), rel, float(np.max(err / allow))
 
 
 def assert_bf16_close(got, ref_f64, rel_tol=TOL_REL_L2, what=""):
-    mx, rel = bf16_errors(got, ref_f64)
-    assert mx <= TOL_MAX_ABS and rel <= rel_tol, f"{what}: max-abs {mx:.3g}, rel-L2 {rel:.3g}"
+    mx, rel, over = bf16_errors(got, ref_f64)
+    assert over <= 1.0 and rel <= rel_tol, f"{what}: max-abs {mx:.3g} ({over:.2f} of allowance), rel-L2 {rel:.3g}"
     return mx, rel
 
 
@@ -65,9 +73,11 @@ class PagedCase:
 
     def __init__(self, w: W.DecodeWorkload, layers: int = None, lens=None, table=None,
                  num_blocks: int = None, poison: bool = True, keep_layers=None, keep_seqs=None):
+        self.lens = np.asarray(lens if lens is not None else W.context_lengths(w), dtype=np.int32)
+        if len(self.lens) != w.b:
+            w = w.with_(b=len(self.lens))     # the batch is the given lengths
         self.w = w
         self.L = layers if layers is not None else w.layers
-        self.lens = np.asarray(lens if lens is not None else W.context_lengths(w), dtype=np.int32)
         if table is None:
             table, nb = W.block_tables(w, self.lens)
         else:

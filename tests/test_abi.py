@@ -129,6 +129,46 @@ def test_decode_dtype_and_layer_errors():
     assert _status("kvd_decode_attn", bf.handle, 0, ctypes.byref(a0), None) == 0
 
 
+def test_partials_argument_errors():
+    pool = _pool()
+    a = _args()
+    assert _status("kvd_decode_partials", pool.handle, 0, ctypes.byref(a), None, FAKE, None) == 1
+    assert _status("kvd_decode_partials", pool.handle, 0, ctypes.byref(a), FAKE, None, None) == 1
+    assert _status("kvd_decode_partials", pool.handle, 0, ctypes.byref(a), FAKE + 4, FAKE, None) == 1
+    sa = _args(score=FAKE, score_stride=100)
+    assert _status("kvd_decode_partials", pool.handle, 0, ctypes.byref(sa), FAKE, FAKE, None) == 1
+    # works on either dtype; an empty batch is a no-op
+    a0 = _args(b=0)
+    assert _status("kvd_decode_partials", _pool(kvd.KVD_FP8_E4M3).handle, 0, ctypes.byref(a0), FAKE, FAKE, None) == 0
+
+
+def test_binding_checks_shapes_before_any_call():
+    import torch
+    b, n_q, d = 2, 8, 128
+    q = torch.zeros((b, n_q, d), dtype=torch.bfloat16)
+    bt = torch.zeros((b, 4), dtype=torch.int32)
+    lens = torch.zeros((b,), dtype=torch.int32)
+    out = torch.zeros_like(q)
+    with pytest.raises(ValueError, match="block_table"):
+        kvd.make_args(q, torch.zeros((3, 4), dtype=torch.int32), lens, 64, out)
+    with pytest.raises(ValueError, match="context_lens"):
+        kvd.make_args(q, bt, torch.zeros((3,), dtype=torch.int32), 64, out)
+    with pytest.raises(ValueError, match="out"):
+        kvd.make_args(q, bt, lens, 64, torch.zeros((b, n_q, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="q must be"):
+        kvd.make_args(q.float(), bt, lens, 64, out)
+    with pytest.raises(ValueError, match="lse_out"):
+        kvd.make_args(q, bt, lens, 64, out, lse_out=torch.zeros((b, n_q + 1)))
+    with pytest.raises(ValueError, match="score"):
+        kvd.make_args(q, bt, lens, 64, out, score=torch.zeros((b + 1, 64)))
+    with pytest.raises(ValueError, match="GPU"):         # host tensors never reach the library
+        kvd.make_args(q, bt, lens, 64, out)
+    with pytest.raises(ValueError, match="one context length"):
+        kvd.slot_mapping_for(bt, torch.zeros((3,), dtype=torch.int32))
+    with pytest.raises(ValueError, match="longer"):
+        kvd.slot_mapping_for(bt, torch.tensor([65, 1], dtype=torch.int32))
+
+
 def test_write_and_merge_argument_errors():
     pool = _pool()
     assert _status("kvd_write_kv", pool.handle, 5, FAKE, FAKE, FAKE, 4, None) == 1
@@ -152,7 +192,8 @@ def _plan(pool, **kw):
 
 def test_plan_and_workspace():
     pool = _pool()
-    # forced chunks: ceil(100 / 32) = 4 chunks; partials b*n_q*4*(128+1) fp32, each region 256-aligned
+    # forced chunks: ceil(100 / 32) = 4 chunks; partials b*n_q*4*(128+1) fp32,
+    # each region 256-aligned
     c, n, ws = _plan(pool, chunk_tokens=32)
     assert (c, n) == (32, 4)
     po = 2 * 8 * 4 * 128 * 4

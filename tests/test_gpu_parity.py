@@ -239,6 +239,41 @@ def test_merge_partials_export(env):
     assert torch.all(out[1, 2] == 0)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("chunk", [0, 48, 128])
+def test_decode_partials_match_oracle_chunks(env, fp8, chunk):
+    kvd, H, W, torch = env
+    from oracle import attention
+    w = _workload(W, 8, 128, fp8=fp8, seed=700)
+    case = _case(H, W, w)
+    part_o, part_lse, C, nc = kvd.kvd_decode_partials(case.pool, 0, case.q[0], case.table_t, case.lens_t,
+                                                      case.max_ctx, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    po, pl = part_o.cpu().double().numpy(), part_lse.cpu().double().numpy()
+    qf = H.bf16_to_f64(case.q[0])
+    for i, s in enumerate(LENS):
+        K, V = case.logical(0, i)
+        oc, lc = attention.chunk_partials(qf[i], K, V, C, n_chunks=nc)
+        live = np.isfinite(lc)
+        assert np.array_equal(np.isneginf(pl[i]), ~live), (i, s)
+        if live.any():
+            err = np.abs(po[i][live] - oc[live]) / np.maximum(1.0, np.abs(oc[live]))
+            assert err.max() <= 1e-5, (i, s, err.max())
+            lerr = np.abs(pl[i][live] - lc[live]) / np.maximum(1.0, np.abs(lc[live]))
+            assert lerr.max() <= 1e-5, (i, s, lerr.max())
+    # merging them reproduces the one-call result bit for bit
+    out = torch.empty_like(case.q[0])
+    lse = torch.empty(case.q[0].shape[:2], dtype=torch.float32, device="cuda")
+    kvd.kvd_merge_partials(part_o, part_lse, out, lse)
+    ref_out, ref_lse = case.run(0, chunk=chunk)
+    torch.cuda.synchronize()
+    if nc > 1:
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+        assert torch.equal(lse, ref_lse)
+    else:
+        H.assert_bf16_close(out, case.oracle(0)[0], what="merged single chunk")
+
+
 def test_bad_block_ids_read_as_zero(env):
     kvd, H, W, torch = env
     w = _workload(W, 4, 64, seed=500)

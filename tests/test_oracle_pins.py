@@ -144,3 +144,15 @@ def test_vectorised_gather_indices_match_scalar_layout():
             for c in (0, 3, 7):
                 assert k_idx[t, j, c] == lay.k_offset(2, p, j, row, c)
                 assert v_idx[t, j, c] == lay.v_offset(2, p, j, row, c)
+
+
+def test_bf16_ulp():
+    from oracle import numerics
+    x = np.array([1.0, 1.5, 1.99, 2.0, 3.0, 0.25, -5.0, 1e-40])
+    exp = np.array([2.0 ** -7, 2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -6, 2.0 ** -9, 2.0 ** -5, 2.0 ** -133])
+    assert np.array_equal(numerics.bf16_ulp(x), exp)
+    # the spacing is the gap to the next bf16 number up
+    bits = np.array([0x3F80, 0x4000, 0x3E80, 0x0001], dtype=np.uint16)
+    v = numerics.bf16_bits_to_f64(bits)
+    nxt = numerics.bf16_bits_to_f64(bits + 1)
+    assert np.array_equal(nxt - v, numerics.bf16_ulp(v))

@@ -101,8 +101,8 @@ def block_tables(w: DecodeWorkload, lens: np.ndarray,
     if num_blocks < total:
         raise ValueError(f"pool of {num_blocks} blocks cannot hold {total}")
     perm = rng.permutation(num_blocks).astype(np.int32)
-    max_blocks = max(max(need), 1)
-    table = np.full((w.b, max_blocks), pad_value, dtype=np.int32)
+    max_blocks = max(max(need, default=0), 1)
+    table = np.full((len(need), max_blocks), pad_value, dtype=np.int32)
     cur = 0
     for i, n in enumerate(need):
         table[i, :n] = perm[cur:cur + n]
