@@ -14,7 +14,8 @@ Reported:
                  exactly K steps bracketed by device synchronisation;
 * seq-steps/s -- sequences x steps per second; % of the 8 TB/s HBM peak;
 * roofline    -- the decode kernel alone: algorithmic bytes per launch over
-                 its mean duration from a HIP event pair around every launch;
+                 its mean duration, from a HIP event pair around a run of
+                 back-to-back launches of it;
 * cpu_baseline-- the float64 oracle timed on a bounded sample on the host.
 
 Timing details: inputs are resident in HBM before the timed region; the step
@@ -189,21 +190,21 @@ class Workload:
         return time.perf_counter() - t0
 
     def time_launches(self, n: int) -> float:
-        """Mean duration (s) of the decode kernel, from a HIP event pair around each
-        launch (a kvd_decode_partials call is exactly one launch of it)."""
+        """Mean duration (s) of the decode kernel: n back-to-back launches of it
+        (kvd_decode_partials calls, each exactly one launch), cycling through
+        replicas and layers, between one HIP event pair on their stream."""
         torch = self.torch
         stream = torch.cuda.current_stream()
         h = int(stream.cuda_stream)
-        evs = []
+        for k in range(min(n, 8)):                       # warm
+            self.call_partials(k % self.R, (k // self.R) % self.w.layers, h)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
         for k in range(n):
-            r, layer = k % self.R, (k // self.R) % self.w.layers
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            self.call_partials(r, layer, h)
-            b.record(stream)
-            evs.append((a, b))
+            self.call_partials(k % self.R, (k // self.R) % self.w.layers, h)
+        b.record(stream)
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in evs) / len(evs) / 1e3
+        return a.elapsed_time(b) / n / 1e3
 
     def config(self):
         w = self.w
@@ -314,6 +315,8 @@ def main():
     ap.add_argument("--launches", type=int, default=200, help="event-timed launches for the roofline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -325,6 +328,22 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+
+    if args.copy_probe:
+        # A plain copy of known size: under rocprofv3 --pmc its FETCH_SIZE and
+        # WRITE_SIZE per dispatch calibrate the counters against known bytes.
+        n = args.copy_probe
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 10
+        print(json.dumps({"copy_bytes": n, "us_per_copy": round(dt * 1e6, 2),
+                          "GBs_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
+        return
 
     wl, head = measure(args.workload, args.chunk, args.replicas, args.steps, args.warmup, args.launches)
     cpu = None

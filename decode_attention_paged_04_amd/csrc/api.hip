@@ -12,11 +12,20 @@ namespace {
 using kvd::DecodePlan;
 using kvd::PoolView;
 
-// Auto split: aim for about this many (sequence, KV head, chunk) workgroups
-// per launch -- several per compute unit on a 256-CU part -- with chunks no
-// shorter than kMinChunk tokens.
-constexpr int64_t kTargetWorkgroups = 1024;
-constexpr int32_t kMinChunk = 256;
+// Automatic split of the context into chunks (one workgroup per (sequence, KV
+// head, chunk)).  With few (sequence, KV head) units -- one long request, or
+// a handful of them -- about one workgroup per compute unit of a 256-CU part
+// streams best: each workgroup keeps its four waves busy on one long run of
+// blocks and the merge has few chunks to combine.  With many units the
+// lengths of a batch usually differ (the host only knows their maximum), so
+// the split aims at about sixteen workgroups per compute unit, sized on the
+// maximum, which evens out short and long sequences.  Chunks are at least
+// kMinChunk tokens and a multiple of kChunkQuantum.  (Measured on MI355X:
+// 8B-shaped single sequence best at 1024 tokens, 70B-shaped 4 x 131k at
+// 16384, 32 ragged 4k..16k sequences at 1024.)
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kManyUnits = 256;
+constexpr int32_t kMinChunk = 1024;
 constexpr int32_t kChunkQuantum = 128;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -53,8 +62,10 @@ kvd_status plan_decode(const PoolView& p, const kvd_decode_args* a, DecodePlan* 
   pl.ctx_bound = (int32_t)bound64;
   int64_t chunk = a->chunk_tokens;
   if (chunk == 0) {
-    const int64_t total = (int64_t)std::max(a->b, 1) * p.n_kv * std::max(pl.ctx_bound, 1);
-    chunk = (total + kTargetWorkgroups - 1) / kTargetWorkgroups;
+    const int64_t units = (int64_t)std::max(a->b, 1) * p.n_kv;
+    const int64_t target = units >= kManyUnits ? 16 * kComputeUnits : kComputeUnits;
+    const int64_t total = units * std::max(pl.ctx_bound, 1);
+    chunk = (total + target - 1) / target;
     chunk = (chunk + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
     chunk = std::max<int64_t>(chunk, kMinChunk);
   }

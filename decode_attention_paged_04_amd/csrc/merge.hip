@@ -10,38 +10,39 @@ namespace kvd {
 constexpr float kLog2eMerge = 1.4426950408889634f;
 constexpr int kMergeThreads = 256;
 
-template <bool MAX>
-__device__ inline float block_reduce(float v, float* red) {
+__device__ inline float wave_max(float v) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float o = __shfl_xor(v, off);
-    v = MAX ? fmaxf(v, o) : v + o;
-  }
-  const int w = threadIdx.x >> 6;
-  __syncthreads();                               // red may still be read by a previous call
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  v = red[0];
-#pragma unroll
-  for (int k = 1; k < kMergeThreads / 64; ++k) v = MAX ? fmaxf(v, red[k]) : v + red[k];
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;
 }
 
-// One workgroup per (sequence, query head).  lse = M + ln(sum_c exp(lse_c - M))
-// with M = max_c lse_c over the first nc chunks; out = sum_c exp(lse_c - lse) *
-// o_c, rounded to bf16.  A chunk whose weight is 0 (lse_c = -inf) is never
-// read, so its o_c may hold anything.  No chunk, or only empty ones: out = 0,
-// lse = -inf.  The thread count splits the chunks into 256 / D interleaved
-// groups, one channel per thread, summed at the end in a fixed order.
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// One workgroup of four waves per (sequence, query head); wave w owns the
+// channels [w*D/4, (w+1)*D/4).  lse = M + ln(sum_c exp(lse_c - M)) with M =
+// max_c lse_c over the first nc chunks; out = sum_c exp(lse_c - lse) * o_c,
+// rounded to bf16.  A chunk whose weight is 0 (lse_c = -inf) is never read, so
+// its o_c may hold anything.  No chunk, or only empty ones: out = 0, lse =
+// -inf.
+// Every wave computes M and the sum itself with shuffles (no LDS, no
+// barrier), and all loads of a batch of up to kBatch chunks per lane are
+// issued before any is used, so a merge of a few dozen chunks costs about one
+// memory round trip.  Lane l of a wave takes channel l % (D/4) and the chunks
+// c = l / (D/4) (mod NG), NG = 256 / D; the NG partial sums of a channel are
+// added with shuffles in a fixed order.
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
     const int32_t* __restrict__ context_lens, int32_t ctx_bound, int32_t chunk, int32_t n_q,
     int32_t n_chunks, uint16_t* __restrict__ out, float* __restrict__ lse_out,
     float* __restrict__ lse2) {
-  constexpr int NG = kMergeThreads / D;
-  __shared__ float red[kMergeThreads / 64];
-  __shared__ float acc_s[kMergeThreads];
+  constexpr int CH = D / 4;                      // channels per wave
+  constexpr int NG = 64 / CH;                    // chunk groups per channel
+  constexpr int kBatch = 16;                     // chunks per lane loaded at once
   const size_t ih = blockIdx.x;
   int nc = n_chunks;
   if (context_lens) {
@@ -51,38 +52,60 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   }
   const float* pl = part_lse + ih * n_chunks;
   const float* po = part_o + ih * n_chunks * D;
-  const int t = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int ch = (threadIdx.x >> 6) * CH + lane % CH;
+  const int grp = lane / CH;
 
+  // first batch of this lane's partial outputs, loaded before the reductions
+  float ov[kBatch];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int c = grp + k * NG;
+    ov[k] = c < nc ? po[(size_t)c * D + ch] : 0.f;
+  }
   float mx = -INFINITY;
-  for (int c = t; c < nc; c += kMergeThreads) mx = fmaxf(mx, pl[c]);
-  const float M = block_reduce<true>(mx, red);
-  const int ch = t % D, grp = t / D;
+  for (int c = lane; c < nc; c += 64) mx = fmaxf(mx, pl[c]);
+  const float M = wave_max(mx);
   if (M == -INFINITY) {
     if (grp == 0) out[ih * D + ch] = 0;
-    if (t == 0) {
+    if (threadIdx.x == 0) {
       if (lse_out) lse_out[ih] = -INFINITY;
       if (lse2) lse2[ih] = -INFINITY;
     }
     return;
   }
   float sm = 0.f;
-  for (int c = t; c < nc; c += kMergeThreads) sm += expf(pl[c] - M);
-  const float lse = M + logf(block_reduce<false>(sm, red));
+  for (int c = lane; c < nc; c += 64) sm += expf(pl[c] - M);
+  const float lse = M + logf(wave_sum(sm));
 
   float acc = 0.f;
-#pragma unroll 8
-  for (int c = grp; c < nc; c += NG) {
-    const float w = expf(pl[c] - lse);
-    if (w != 0.f) acc += w * po[(size_t)c * D + ch];
-  }
-  acc_s[t] = acc;
-  __syncthreads();
-  if (grp == 0) {
 #pragma unroll
-    for (int k = 1; k < NG; ++k) acc += acc_s[k * D + ch];
-    out[ih * D + ch] = float_to_bf16_bits(acc);
+  for (int k = 0; k < kBatch; ++k) {
+    const int c = grp + k * NG;
+    if (c < nc) {
+      const float w = expf(pl[c] - lse);
+      if (w != 0.f) acc += w * ov[k];
+    }
   }
-  if (t == 0) {
+  for (int c0 = kBatch * NG; c0 < nc; c0 += kBatch * NG) {   // long splits: further batches
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int c = c0 + grp + k * NG;
+      ov[k] = c < nc ? po[(size_t)c * D + ch] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int c = c0 + grp + k * NG;
+      if (c < nc) {
+        const float w = expf(pl[c] - lse);
+        if (w != 0.f) acc += w * ov[k];
+      }
+    }
+  }
+#pragma unroll
+  for (int off = CH; off < 64; off <<= 1) acc += __shfl_xor(acc, off);
+  if (grp == 0) out[ih * D + ch] = float_to_bf16_bits(acc);
+  if (threadIdx.x == 0) {
     if (lse_out) lse_out[ih] = lse;
     if (lse2) lse2[ih] = lse * kLog2eMerge;
   }
