@@ -63,8 +63,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const int c = grp + k * NG;
     ov[k] = c < nc ? po[(size_t)c * D + ch] : 0.f;
   }
-  float mx = -INFINITY;
-  for (int c = lane; c < nc; c += 64) mx = fmaxf(mx, pl[c]);
+  // lane c holds lse_c of the first 64 chunks; more chunks are looped over
+  const float lv = lane < nc ? pl[lane] : -INFINITY;
+  float mx = lv;
+  for (int c = lane + 64; c < nc; c += 64) mx = fmaxf(mx, pl[c]);
   const float M = wave_max(mx);
   if (M == -INFINITY) {
     if (grp == 0) out[ih * D + ch] = 0;
@@ -74,18 +76,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     }
     return;
   }
-  float sm = 0.f;
-  for (int c = lane; c < nc; c += 64) sm += expf(pl[c] - M);
+  float sm = lane < nc ? expf(lv - M) : 0.f;
+  for (int c = lane + 64; c < nc; c += 64) sm += expf(pl[c] - M);
   const float lse = M + logf(wave_sum(sm));
+  // each lane's weight exp(lse_c - lse) for c = lane, shared by shuffles below
+  const float wl = lane < nc ? expf(lv - lse) : 0.f;
 
   float acc = 0.f;
 #pragma unroll
   for (int k = 0; k < kBatch; ++k) {
-    const int c = grp + k * NG;
-    if (c < nc) {
-      const float w = expf(pl[c] - lse);
-      if (w != 0.f) acc += w * ov[k];
-    }
+    const int c = grp + k * NG;                    // < 64: its weight sits in lane c
+    const float w = __shfl(wl, c);
+    if (c < nc && w != 0.f) acc += w * ov[k];
   }
   for (int c0 = kBatch * NG; c0 < nc; c0 += kBatch * NG) {   // long splits: further batches
 #pragma unroll
