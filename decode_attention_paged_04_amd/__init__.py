@@ -119,7 +119,7 @@ class Pool:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
+        if h and lib is not None:          # at interpreter exit the module may be gone
             lib.kvd_destroy_pool(h)
             self.handle = None
 
