@@ -56,6 +56,9 @@ kvd_status plan_decode(const PoolView& p, const kvd_decode_args* a, DecodePlan* 
   if (a->chunk_tokens < 0 || a->chunk_tokens % kvd::kBlock != 0) return KVD_ERR_INVALID_ARG;
   if (a->score && (a->score_stride < 1 || a->score_stride < a->max_context_len))
     return KVD_ERR_INVALID_ARG;
+  // With a score every chunk must cover whole 32-token pairs: a pair's score
+  // slots must not reach into the next chunk's.
+  if (a->score && a->chunk_tokens % 32 != 0) return KVD_ERR_INVALID_ARG;
   DecodePlan pl{};
   const int64_t bound64 = std::min<int64_t>(a->max_context_len, (int64_t)kvd::kBlock * a->max_blocks_per_seq);
   if (bound64 > (int64_t)1 << 30) return KVD_ERR_UNSUPPORTED;

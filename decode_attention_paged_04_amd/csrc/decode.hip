@@ -124,8 +124,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeLaunch a) 
   auto issue = [&](R& f, int p) {
     const bool live = p < npairs;
     const int nvalid = min(32, ntok - (p << 5));
-    const int32_t pid0 = live ? bt[2 * p] : -1;
-    const int32_t pid1 = live && nvalid > kBlock ? bt[2 * p + 1] : -1;
+    const int32_t pid0 = live ? load_invariant(bt + 2 * p) : -1;
+    const int32_t pid1 = live && nvalid > kBlock ? load_invariant(bt + 2 * p + 1) : -1;
     const uint32_t t0 = tile_pair_offset(pid0, j, a.num_blocks, a.n_kv, TPB);
     const uint32_t t1 = tile_pair_offset(pid1, j, a.num_blocks, a.n_kv, TPB);
     // K: S-tile t, row r16 -> block r16/8, in-block row 8*((r16/4)&1) + 4t + r16%4;
@@ -153,10 +153,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeLaunch a) 
     if constexpr (FP8) {
       // fp32 scales of this lane's block (G/2) for K and V; zero for a bad id.
       const float* sc = a.layer_scales;
-      const float sk0 = t0 == kOutOfRange ? 0.f : sc[((size_t)pid0 * a.n_kv + j) * 2 + 0];
-      const float sv0 = t0 == kOutOfRange ? 0.f : sc[((size_t)pid0 * a.n_kv + j) * 2 + 1];
-      const float sk1 = t1 == kOutOfRange ? 0.f : sc[((size_t)pid1 * a.n_kv + j) * 2 + 0];
-      const float sv1 = t1 == kOutOfRange ? 0.f : sc[((size_t)pid1 * a.n_kv + j) * 2 + 1];
+      const float sk0 = t0 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid0 * a.n_kv + j) * 2 + 0);
+      const float sv0 = t0 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid0 * a.n_kv + j) * 2 + 1);
+      const float sk1 = t1 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid1 * a.n_kv + j) * 2 + 0);
+      const float sv1 = t1 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid1 * a.n_kv + j) * 2 + 1);
       f.sK = G < 2 ? sk0 : sk1;
       f.sV = G < 2 ? sv0 : sv1;
     }
@@ -200,10 +200,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeLaunch a) 
     }
 
     if constexpr (SCORES) {
+      // Scaled scores of this head and pair, stored pair-permuted (see
+      // score_slot): the lanes' first halves form one contiguous 64-byte run,
+      // their second halves the next, so each store instruction writes whole
+      // runs.
       if (head_ok) {
-        float* dst = a.logits + ih * a.logit_stride + lo + tok0 + 8 * G;
+        float* dst = a.logits + ih * a.logit_stride + lo + tok0 + 4 * G;
         *reinterpret_cast<f32x4*>(dst) = f32x4{xs[0], xs[1], xs[2], xs[3]};
-        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{xs[4], xs[5], xs[6], xs[7]};
+        *reinterpret_cast<f32x4*>(dst + 16) = f32x4{xs[4], xs[5], xs[6], xs[7]};
       }
     }
 

@@ -38,6 +38,16 @@ __device__ inline u32x2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kStreamPolicy));
 }
 
+// Read of memory that no kernel writes while this one runs (block tables,
+// scales).  Through the constant address space a wave-uniform address becomes a
+// scalar load, whose wait (lgkmcnt) is independent of the vector loads and
+// stores in flight; a vector load here would need vmcnt(0) before its
+// readfirstlane and so drain every K/V load of the wave.
+template <typename T>
+__device__ inline T load_invariant(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // Byte offset, from the start of a layer, of the tile pair of (block p, KV head
 // j); kOutOfRange for a block id outside the pool, so every load through it
 // reads zeros.

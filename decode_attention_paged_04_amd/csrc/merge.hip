@@ -113,23 +113,42 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   }
 }
 
+// Slot of token t in the score scratch.  Within each 32-token pair the decode
+// kernel holds tokens 8G .. 8G+7 in lane group G and stores the first four of
+// every group, then the last four: token 8G + 4h + e goes to slot 16h + 4G + e.
+__device__ inline int score_slot(int t) {
+  const int r = t & 31;
+  return (t & ~31) + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+}
+
 // score[i][t] += weight / n_q * sum_h exp2(x[i][h][t] - lse2[i][h]) for t < s_i,
-// x being the log2-domain scaled scores the decode kernel stored.
+// x being the log2-domain scaled scores the decode kernel stored.  Each thread
+// owns one token; the heads' loads are issued eight at a time so that they are
+// in flight together, and the sum runs in head order.
 __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ logits,
                                                     const float* __restrict__ lse2,
                                                     const int32_t* __restrict__ context_lens,
                                                     int32_t ctx_bound, int32_t n_q,
                                                     int32_t stride, float* __restrict__ score,
                                                     int32_t score_stride, float w_over_nq) {
+  constexpr int U = 8;
   const int i = blockIdx.y;
   const int t = blockIdx.x * 256 + threadIdx.x;
   int s = context_lens[i];
   s = s < 0 ? 0 : (s > ctx_bound ? ctx_bound : s);
   if (t >= s) return;
-  const float* x = logits + (size_t)i * n_q * stride + t;
+  const float* x = logits + (size_t)i * n_q * stride + score_slot(t);
   const float* ls = lse2 + (size_t)i * n_q;
   float acc = 0.f;
-  for (int h = 0; h < n_q; ++h) acc += __builtin_amdgcn_exp2f(x[(size_t)h * stride] - ls[h]);
+  int h = 0;
+  for (; h + U <= n_q; h += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = x[(size_t)(h + u) * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += __builtin_amdgcn_exp2f(v[u] - ls[h + u]);
+  }
+  for (; h < n_q; ++h) acc += __builtin_amdgcn_exp2f(x[(size_t)h * stride] - ls[h]);
   score[(size_t)i * score_stride + t] += w_over_nq * acc;
 }
 

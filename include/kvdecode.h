@@ -131,6 +131,7 @@ typedef struct {
   float* lse_out;             /* optional device fp32 [b][n_q]: natural-log           */
                               /* log-sum-exp of the scaled scores (-inf if s_i = 0)   */
   int32_t chunk_tokens;       /* context split: 0 = automatic, else a multiple of 16  */
+                              /* (of 32 when a score is requested)                    */
   void* workspace;            /* device scratch of kvd_decode_workspace_bytes bytes,  */
   size_t workspace_bytes;     /* 256-byte aligned; may be NULL when that size is 0.   */
                               /* Calls that overlap in time must not share one.       */

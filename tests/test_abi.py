@@ -105,6 +105,7 @@ def _args(**kw):
     (dict(b=-1), 1), (dict(max_blocks_per_seq=0), 1), (dict(max_context_len=-5), 1),
     (dict(q=None), 1), (dict(block_table=None), 1), (dict(context_lens=None), 1), (dict(out=None), 1),
     (dict(score=FAKE, score_stride=50), 1),      # stride shorter than the context bound
+    (dict(score=FAKE, score_stride=100, chunk_tokens=48), 1),   # scores need whole 32-token pairs
     (dict(chunk_tokens=16), 4),            # needs a workspace, none given
     (dict(chunk_tokens=16, workspace=FAKE, workspace_bytes=16), 4),
     (dict(chunk_tokens=16, workspace=FAKE + 16, workspace_bytes=1 << 30), 4),   # misaligned

@@ -295,7 +295,7 @@ def test_bad_block_ids_read_as_zero(env):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("chunk", [0, 64])
+@pytest.mark.parametrize("chunk", [0, 32, 64, 96])
 def test_fused_cumulative_scores(env, fp8, chunk):
     kvd, H, W, torch = env
     w = _workload(W, 4, 128, fp8=fp8, seed=600, layers=3)
