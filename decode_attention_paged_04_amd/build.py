@@ -19,6 +19,8 @@ FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-shared",
+    # every symbol resolved at link time, not at load time on the device host
+    "-Wl,-z,defs",
     "-Wall",
     # correctly rounded fp32 division and sqrt (the FP8 codes depend on them)
     "-fhip-fp32-correctly-rounded-divide-sqrt",
