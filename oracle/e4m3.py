@@ -17,6 +17,13 @@ multiplied by it when read.  Readings taken here:
   filled rows, computed as an IEEE fp32 division, and y = x / scale also in
   fp32 (the precision in which the integer code is decided).  An all-zero
   block gets scale 0 and all-zero codes.
+* Appending rows to a partly filled tile (a decode step adds one token to
+  the last block) keeps one scale per tile: the new scale is absmax / 448
+  over the old rows as they read back (code value times old scale, an fp32
+  product) together with the new rows; the old codes are re-encoded from
+  those read-back values only when the scale changed, and the new rows are
+  encoded under the new scale.  Appending to an empty tile is the plain
+  block quantisation above.
 """
 from __future__ import annotations
 
@@ -99,6 +106,57 @@ def quantize_tile(x_rows, scale: np.float32) -> np.ndarray:
     if scale == 0:
         return np.zeros(x.shape, dtype=np.uint8)
     return encode(x / np.float32(scale))
+
+
+def append_tile(codes, scale, x_new):
+    """Append rows to one (block, head) tile and re-quantise it.
+
+    ``codes`` are the tile's filled rows ``[r0][d]`` (uint8, r0 may be 0),
+    ``scale`` its fp32 scale, ``x_new`` the appended rows ``[n][d]``.
+    Returns the codes of all ``r0 + n`` rows and the tile's new scale.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    x_new = np.asarray(x_new, dtype=np.float32)
+    old = decode_table()[codes].astype(np.float32) * np.float32(scale)   # read-back values, fp32
+    both = np.concatenate([old.reshape(-1), x_new.reshape(-1)])
+    absmax = np.float32(np.max(np.abs(both))) if both.size else np.float32(0)
+    new_scale = np.float32(scale_of_absmax(absmax))
+    if codes.shape[0] and new_scale != np.float32(scale):
+        codes = quantize_tile(old, new_scale)
+    return np.concatenate([codes, quantize_tile(x_new, new_scale)]), new_scale
+
+
+def append_sequence(codes, scales, X_new):
+    """Append tokens to one sequence's quantised K (or V).
+
+    ``codes`` ``[s][n_kv][d]`` and ``scales`` ``[ceil(s/16)][n_kv]`` describe
+    the sequence as stored so far; ``X_new`` ``[n][n_kv][d]`` are the next
+    tokens.  Each touched block and head goes through :func:`append_tile` once
+    with all of its new rows.  Returns the updated codes and scales.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.float32)
+    X_new = np.asarray(X_new, dtype=np.float32)
+    s, n = codes.shape[0], X_new.shape[0]
+    n_kv, d = X_new.shape[1], X_new.shape[2]
+    total = s + n
+    nb = -(-total // BLOCK_SIZE)
+    out_codes = np.zeros((total, n_kv, d), dtype=np.uint8)
+    out_codes[:s] = codes
+    out_scales = np.zeros((nb, n_kv), dtype=np.float32)
+    out_scales[:scales.shape[0]] = scales
+    t = s
+    while t < total:
+        blk = t // BLOCK_SIZE
+        r0 = t - blk * BLOCK_SIZE
+        end = min(total, (blk + 1) * BLOCK_SIZE)
+        for j in range(n_kv):
+            tile, sc = append_tile(out_codes[blk * BLOCK_SIZE:t, j], out_scales[blk, j],
+                                   X_new[t - s:end - s, j])
+            out_codes[blk * BLOCK_SIZE:end, j] = tile
+            out_scales[blk, j] = sc
+        t = end
+    return out_codes, out_scales
 
 
 def quantize_sequence(X: np.ndarray):

@@ -378,3 +378,66 @@ def fp8_quant_failures(seed=8) -> list:
     if sY[0, 0] != 1.0 or not np.array_equal(e4m3.dequantize_sequence(cY, sY)[0, 0], Y[0, 0]):
         bad.append("exact")
     return bad
+
+
+def fp8_append_failures(seed=9) -> list:
+    """Appending to partly filled FP8 tiles: reduces to the block quantiser when
+    a tile starts empty; scales only grow; the largest element of a nonzero
+    tile reads back as +-448; appended rows, and old rows across a re-encode,
+    move by at most half an E4M3 step; zero rows leave a tile untouched; on a
+    power-of-two grid every value survives a scale doubling exactly."""
+    rng = np.random.default_rng(seed)
+    bad = []
+    table = e4m3.decode_table()
+    s, n_kv, d = 37, 2, 8
+    X = (rng.standard_normal((s, n_kv, d)) * 3).astype(np.float32)
+    X[20, 0, 3] = 40.0                           # a late large value forces a re-encode
+    empty_c = np.zeros((0, n_kv, d), np.uint8)
+    empty_s = np.zeros((0, n_kv), np.float32)
+    # whole sequence in one append == block quantisation
+    c_all, s_all = e4m3.append_sequence(empty_c, empty_s, X)
+    c_ref, s_ref = e4m3.quantize_sequence(X)
+    if not (np.array_equal(c_all, c_ref) and np.array_equal(s_all, s_ref)):
+        bad.append("prefill")
+    # token by token after a 5-token prefill
+    c, sc = e4m3.append_sequence(empty_c, empty_s, X[:5])
+    half = 2.0 ** -4 + 1e-6                      # half a step relative, plus fp32 slack
+    for t in range(5, s):
+        before = e4m3.dequantize_sequence(c, sc)
+        c2, sc2 = e4m3.append_sequence(c, sc, X[t:t + 1])
+        after = e4m3.dequantize_sequence(c2, sc2)
+        nb_old = sc.shape[0]
+        if np.any(sc2[:nb_old] < sc):
+            bad.append(("monotone", t))
+        blk = t // 16
+        for j in range(n_kv):
+            tile = c2[blk * 16:t + 1, j]
+            if sc2[blk, j] != 0 and np.max(np.abs(table[tile])) != 448.0:
+                bad.append(("max448", t, j))
+        floor = 2.0 ** -6 * np.float64(sc2[blk])[None, :, None]    # below: subnormal grid
+        rows = slice(blk * 16, t)
+        o_b, o_a = before[rows], after[rows]
+        big = np.abs(o_b) >= floor
+        if np.any(np.abs(o_a - o_b)[big] > half * np.abs(o_b)[big]):
+            bad.append(("old_moved", t))
+        if np.any(np.abs(o_a - o_b)[~big] > 2.0 ** -10 * np.broadcast_to(np.float64(sc2[blk])[None, :, None], o_b.shape)[~big] + 1e-30):
+            bad.append(("old_moved_sub", t))
+        x = X[t].astype(np.float64)
+        bigx = np.abs(x) >= floor[0]
+        if np.any(np.abs(after[t] - x)[bigx] > half * np.abs(x)[bigx]):
+            bad.append(("new_row", t))
+        c, sc = c2, sc2
+    # zero rows appended under an unchanged scale leave the old codes as they are
+    base_c, base_s = e4m3.append_sequence(empty_c, empty_s, X[:3])
+    zc, zs = e4m3.append_sequence(base_c, base_s, np.zeros((2, n_kv, d), np.float32))
+    if np.array_equal(zs, base_s) and not np.array_equal(zc[:3], base_c):
+        bad.append("zero_append")
+    # power-of-two grid: scale 1 then 2, every value read back exactly
+    g = np.array([[448.0, -3.25, 0.125, 2.0 ** -5]], np.float32).reshape(1, 1, 4)
+    gc, gs = e4m3.append_sequence(np.zeros((0, 1, 4), np.uint8), np.zeros((0, 1), np.float32), g)
+    g2 = np.array([[896.0, 1.0, -6.5, 0.25]], np.float32).reshape(1, 1, 4)
+    gc2, gs2 = e4m3.append_sequence(gc, gs, g2)
+    back = e4m3.dequantize_sequence(gc2, gs2)
+    if gs[0, 0] != 1.0 or gs2[0, 0] != 2.0 or not np.array_equal(back, np.concatenate([g, g2]).astype(np.float64)):
+        bad.append("grid")
+    return bad

@@ -27,7 +27,8 @@ def _all_pins_pass() -> bool:
             and pins.block_table_example_failures() == []
             and pins.placement_invariance_max_error() == 0.0
             and pins.score_failures() == []
-            and pins.fp8_quant_failures() == [])
+            and pins.fp8_quant_failures() == []
+            and pins.fp8_append_failures() == [])
 
 
 def _modulo_heads(h, n_q, n_kv):
@@ -108,6 +109,40 @@ def _scale_over_256(absmax):
     return (np.asarray(absmax, dtype=np.float32) / np.float32(256.0)).astype(np.float32)
 
 
+def _append_absmax_new_rows_only(codes, scale, x_new):
+    codes = np.asarray(codes, dtype=np.uint8)
+    x_new = np.asarray(x_new, dtype=np.float32)
+    old = e4m3.decode_table()[codes].astype(np.float32) * np.float32(scale)
+    am = np.float32(np.max(np.abs(x_new))) if x_new.size else np.float32(0)
+    ns = np.float32(e4m3.scale_of_absmax(am))
+    if codes.shape[0] and ns != np.float32(scale):
+        codes = e4m3.quantize_tile(old, ns)
+    return np.concatenate([codes, e4m3.quantize_tile(x_new, ns)]), ns
+
+
+def _append_never_reencodes(codes, scale, x_new):
+    codes = np.asarray(codes, dtype=np.uint8)
+    x_new = np.asarray(x_new, dtype=np.float32)
+    old = e4m3.decode_table()[codes].astype(np.float32) * np.float32(scale)
+    both = np.concatenate([old.reshape(-1), x_new.reshape(-1)])
+    am = np.float32(np.max(np.abs(both))) if both.size else np.float32(0)
+    ns = np.float32(e4m3.scale_of_absmax(am))
+    return np.concatenate([codes, e4m3.quantize_tile(x_new, ns)]), ns
+
+
+def _append_new_rows_old_scale(codes, scale, x_new):
+    codes = np.asarray(codes, dtype=np.uint8)
+    x_new = np.asarray(x_new, dtype=np.float32)
+    old = e4m3.decode_table()[codes].astype(np.float32) * np.float32(scale)
+    both = np.concatenate([old.reshape(-1), x_new.reshape(-1)])
+    am = np.float32(np.max(np.abs(both))) if both.size else np.float32(0)
+    ns = np.float32(e4m3.scale_of_absmax(am))
+    enc_scale = np.float32(scale) if codes.shape[0] else ns
+    if codes.shape[0] and ns != np.float32(scale):
+        codes = e4m3.quantize_tile(old, ns)
+    return np.concatenate([codes, e4m3.quantize_tile(x_new, enc_scale)]), ns
+
+
 MUTATIONS = [
     ("heads modulo instead of grouped", attention, "head_group", _modulo_heads),
     ("logit scale dropped", attention, "logits", _no_scale_logits),
@@ -122,6 +157,9 @@ MUTATIONS = [
     ("score missing head mean", scores, "layer_increment", _layer_inc_no_head_mean),
     ("score step missing head mean", scores, "step_increment", _step_inc_no_head_mean),
     ("fp8 scale absmax/256", e4m3, "scale_of_absmax", _scale_over_256),
+    ("fp8 append absmax of new rows only", e4m3, "append_tile", _append_absmax_new_rows_only),
+    ("fp8 append keeps stale codes", e4m3, "append_tile", _append_never_reencodes),
+    ("fp8 append encodes new rows with old scale", e4m3, "append_tile", _append_new_rows_old_scale),
 ]
 
 
