@@ -22,8 +22,8 @@ STATUS = {0: "KVD_OK", 1: "KVD_ERR_INVALID_ARG", 2: "KVD_ERR_UNSUPPORTED", 3: "K
 
 
 class KvdError(RuntimeError):
-    def __init__(self, status: int, where: str):
-        super().__init__(f"{where}: {STATUS.get(status, status)}")
+    def __init__(self, status: int, where: str, detail: str = ""):
+        super().__init__(f"{where}: {STATUS.get(status, status)}" + (f" ({detail})" if detail else ""))
         self.status = status
 
 
@@ -60,6 +60,7 @@ EXPORTS = {
     "kvd_merge_partials": (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p),
     "kvd_status_string": (ctypes.c_int,),
+    "kvd_last_hip_error": (),
     "kvd_debug_gather_offsets": (ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p),
@@ -74,7 +75,7 @@ def _load():
     for name, argtypes in EXPORTS.items():
         fn = getattr(lib, name)
         fn.argtypes = list(argtypes)
-        fn.restype = ctypes.c_char_p if name == "kvd_status_string" else ctypes.c_int
+        fn.restype = ctypes.c_char_p if name in ("kvd_status_string", "kvd_last_hip_error") else ctypes.c_int
     return lib
 
 
@@ -83,7 +84,8 @@ lib = _load()
 
 def _check(st: int, where: str):
     if st != 0:
-        raise KvdError(st, where)
+        detail = lib.kvd_last_hip_error().decode() if st == 5 else ""
+        raise KvdError(st, where, detail)
 
 
 def _ptr(t) -> Optional[int]:

@@ -1,4 +1,5 @@
 // C ABI of libkvdecode: validation, pool layout, launch planning, workspace.
+#include <cstdio>
 #include <new>
 
 #include "kvd_internal.h"
@@ -34,6 +35,18 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // left behind by an earlier, unrelated runtime call in this thread; clear that
 // first so that only this call's launches are judged.
 void clear_stale_error() { (void)hipGetLastError(); }
+
+// HIP error behind the calling thread's most recent KVD_ERR_HIP (errno-like).
+thread_local hipError_t t_last_hip = hipSuccess;
+
+#define KVD_TRY_HIP(call)         \
+  do {                            \
+    const hipError_t e_ = (call); \
+    if (e_ != hipSuccess) {       \
+      t_last_hip = e_;            \
+      return KVD_ERR_HIP;         \
+    }                             \
+  } while (0)
 
 kvd_status check_desc(const kvd_pool_desc* d) {
   if (!d) return KVD_ERR_INVALID_ARG;
@@ -155,18 +168,15 @@ kvd_status decode_common(const kvd_pool* pool, int32_t layer, const kvd_decode_a
   L.logit_stride = pl.logit_stride;
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_stale_error();
-  if (kvd::launch_decode(L, p.head_dim, p.dtype == KVD_FP8_E4M3, final_direct, scores, s) != hipSuccess)
-    return KVD_ERR_HIP;
+  KVD_TRY_HIP(kvd::launch_decode(L, p.head_dim, p.dtype == KVD_FP8_E4M3, final_direct, scores, s));
   if (external) return KVD_OK;
   if (!final_direct) {
-    if (kvd::launch_merge(L.part_o, L.part_lse, a->context_lens, pl.ctx_bound, pl.chunk, a->b,
-                          a->n_q, pl.n_chunks, p.head_dim, L.out, a->lse_out, L.lse2, s) != hipSuccess)
-      return KVD_ERR_HIP;
+    KVD_TRY_HIP(kvd::launch_merge(L.part_o, L.part_lse, a->context_lens, pl.ctx_bound, pl.chunk, a->b,
+                          a->n_q, pl.n_chunks, p.head_dim, L.out, a->lse_out, L.lse2, s));
   }
   if (scores) {
-    if (kvd::launch_score(L.logits, L.lse2, a->context_lens, pl.ctx_bound, a->b, a->n_q,
-                          pl.logit_stride, a->score, a->score_stride, a->score_weight, s) != hipSuccess)
-      return KVD_ERR_HIP;
+    KVD_TRY_HIP(kvd::launch_score(L.logits, L.lse2, a->context_lens, pl.ctx_bound, a->b, a->n_q,
+                          pl.logit_stride, a->score, a->score_stride, a->score_weight, s));
   }
   return KVD_OK;
 }
@@ -226,9 +236,8 @@ kvd_status kvd_write_kv(const kvd_pool* pool, int32_t layer, const void* k, cons
   if (!k || !v || !slot_mapping) return KVD_ERR_INVALID_ARG;
   if ((int64_t)n_tok * pool->v.n_kv * pool->v.head_dim >= ((int64_t)1 << 40)) return KVD_ERR_UNSUPPORTED;
   clear_stale_error();
-  if (kvd::launch_write(pool->v, layer, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                        slot_mapping, n_tok, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
-    return KVD_ERR_HIP;
+  KVD_TRY_HIP(kvd::launch_write(pool->v, layer, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                        slot_mapping, n_tok, static_cast<hipStream_t>(hip_stream)));
   return KVD_OK;
 }
 
@@ -276,11 +285,16 @@ kvd_status kvd_merge_partials(const float* part_o, const float* part_lse, int32_
   if (!part_o || !part_lse || !out_bf16) return KVD_ERR_INVALID_ARG;
   if ((int64_t)b * n_q >= ((int64_t)1 << 31)) return KVD_ERR_UNSUPPORTED;
   clear_stale_error();
-  if (kvd::launch_merge(part_o, part_lse, nullptr, 0, 1, b, n_q, n_chunks, d_h,
+  KVD_TRY_HIP(kvd::launch_merge(part_o, part_lse, nullptr, 0, 1, b, n_q, n_chunks, d_h,
                         static_cast<uint16_t*>(out_bf16), lse_out, nullptr,
-                        static_cast<hipStream_t>(hip_stream)) != hipSuccess)
-    return KVD_ERR_HIP;
+                        static_cast<hipStream_t>(hip_stream)));
   return KVD_OK;
+}
+
+const char* kvd_last_hip_error(void) {
+  thread_local char buf[160];
+  snprintf(buf, sizeof buf, "%s: %s", hipGetErrorName(t_last_hip), hipGetErrorString(t_last_hip));
+  return buf;
 }
 
 const char* kvd_status_string(kvd_status s) {
@@ -304,9 +318,8 @@ kvd_status kvd_debug_gather_offsets(const kvd_pool* pool, int32_t layer, const i
   if ((int64_t)b * n_tok == 0) return KVD_OK;
   if (!block_table || !out_k || !out_v) return KVD_ERR_INVALID_ARG;
   clear_stale_error();
-  if (kvd::launch_debug_offsets(pool->v, layer, block_table, max_blocks_per_seq, b, n_tok, out_k, out_v,
-                                static_cast<hipStream_t>(hip_stream)) != hipSuccess)
-    return KVD_ERR_HIP;
+  KVD_TRY_HIP(kvd::launch_debug_offsets(pool->v, layer, block_table, max_blocks_per_seq, b, n_tok, out_k, out_v,
+                                static_cast<hipStream_t>(hip_stream)));
   return KVD_OK;
 }
 
@@ -315,8 +328,7 @@ kvd_status kvd_debug_fp8_decode(const uint8_t* codes, int32_t n, float* out, voi
   if (n == 0) return KVD_OK;
   if (!codes || !out) return KVD_ERR_INVALID_ARG;
   clear_stale_error();
-  if (kvd::launch_debug_fp8_decode(codes, n, out, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
-    return KVD_ERR_HIP;
+  KVD_TRY_HIP(kvd::launch_debug_fp8_decode(codes, n, out, static_cast<hipStream_t>(hip_stream)));
   return KVD_OK;
 }
 

@@ -52,8 +52,19 @@ __device__ inline uint32_t e4m3_encode(float y) {
   return sign | code;
 }
 
-// One wave per (run of consecutive slots starting at a block's row 0, KV head,
-// K|V): absmax over the run, scale = absmax / 448, codes of x / scale.
+// Widen one E4M3FN code to fp32 with the conversion the decode kernels use
+// (exact: every E4M3FN value is a bf16 value).
+__device__ inline float e4m3_to_float(uint32_t code) {
+  return (float)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, false)[0];
+}
+
+// One wave per (run, KV head, K|V).  A run is a maximal stretch of entries of
+// the slot mapping that fill consecutive rows r0, r0+1, ... of one block; rows
+// below r0 already hold codes under the tile's current scale.  The tile keeps
+// one scale: absmax / 448 over the old rows as they read back (code value x old
+// scale, fp32) and the run's new rows.  Old codes are re-encoded from their
+// read-back values only if the scale changed; new rows are encoded under the
+// new scale.  A run starting at row 0 is the plain block quantisation.
 template <int D>
 __global__ __launch_bounds__(64) void write_fp8_kernel(char* __restrict__ layer_base,
                                                        float* __restrict__ layer_scales,
@@ -67,30 +78,46 @@ __global__ __launch_bounds__(64) void write_fp8_kernel(char* __restrict__ layer_
   const int which = blockIdx.z;                     // 0: K, 1: V
   const int lane = threadIdx.x;
   const int32_t slot = slots[t];
-  if (slot < 0 || (slot % kBlock) != 0) return;
+  if (slot < 0) return;
   const int32_t p = slot / kBlock;
   if (p >= num_blocks) return;
+  const int r0 = slot % kBlock;
+  // Only the first entry of a run does the work.
+  if (r0 != 0 && t > 0 && slots[t - 1] == slot - 1) return;
   int n = 1;
-  while (n < kBlock && t + n < n_tok && slots[t + n] == slot + n) ++n;
+  while (r0 + n < kBlock && t + n < n_tok && slots[t + n] == slot + n) ++n;
 
   const uint16_t* src = (which ? v : k) + ((size_t)t * n_kv + j) * D;
   const size_t row_stride = (size_t)n_kv * D;
+  uint8_t* tile = reinterpret_cast<uint8_t*>(layer_base + ((size_t)p * n_kv + j) * (2 * kBlock * D));
+  float* scale_at = layer_scales + ((size_t)p * n_kv + j) * 2 + which;
+  auto at = [&](int r, int ch) -> uint8_t& { return tile[which ? v_elem(r, ch, D) : k_elem(r, ch, D)]; };
+
+  const float s_old = r0 > 0 ? *scale_at : 0.f;
   float am = 0.f;
+  for (int r = 0; r < r0; ++r)
+    for (int ch = lane; ch < D; ch += 64) am = fmaxf(am, fabsf(e4m3_to_float(at(r, ch)) * s_old));
   for (int r = 0; r < n; ++r)
     for (int ch = lane; ch < D; ch += 64) am = fmaxf(am, fabsf(bf16_bits_to_float(src[r * row_stride + ch])));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
   const float scale = am / 448.0f;
 
-  uint8_t* tile = reinterpret_cast<uint8_t*>(layer_base + ((size_t)p * n_kv + j) * (2 * kBlock * D));
+  if (r0 > 0 && scale != s_old) {
+    for (int r = 0; r < r0; ++r) {
+      for (int ch = lane; ch < D; ch += 64) {
+        const float x = e4m3_to_float(at(r, ch)) * s_old;
+        at(r, ch) = (uint8_t)(scale == 0.f ? 0u : e4m3_encode(x / scale));
+      }
+    }
+  }
   for (int r = 0; r < n; ++r) {
     for (int ch = lane; ch < D; ch += 64) {
       const float x = bf16_bits_to_float(src[r * row_stride + ch]);
-      const uint32_t code = scale == 0.f ? 0u : e4m3_encode(x / scale);
-      tile[which ? v_elem(r, ch, D) : k_elem(r, ch, D)] = (uint8_t)code;
+      at(r0 + r, ch) = (uint8_t)(scale == 0.f ? 0u : e4m3_encode(x / scale));
     }
   }
-  if (lane == 0) layer_scales[((size_t)p * n_kv + j) * 2 + which] = scale;
+  if (lane == 0) *scale_at = scale;
 }
 
 hipError_t launch_write(const PoolView& pv, int32_t layer, const uint16_t* k, const uint16_t* v,

@@ -102,15 +102,22 @@ kvd_status kvd_destroy_pool(kvd_pool* pool);
  *   slot / 16, in-block row slot % 16.  Negative slots are skipped (padding),
  *   as are slots past the pool.
  * bf16 pools: a plain copy into the layout.
- * FP8 pools: every (block, KV head) gets one scale for K and one for V,
- *   scale = absmax / 448 over the block's rows written by this call (fp32,
- *   IEEE division), and each element is stored as the nearest-even E4M3 code
- *   of x / scale (fp32 division), saturated to +-448; an all-zero tile gets
- *   scale 0 and zero codes.  (Scale per block and head, not per layer as the
- *   FP8 paragraph of froggydisk's page suggests.)  A block must be written
- *   from row 0 by consecutive entries of one call (slot, slot+1, ...), the
- *   way a prompt is stored; entries that continue a block written by an
- *   earlier call are skipped (appending with re-quantisation is not built).
+ * FP8 pools: every (block, KV head) keeps one scale for K and one for V, and
+ *   each element is stored as the nearest-even E4M3 code of x / scale (fp32
+ *   division), saturated to +-448; an all-zero tile has scale 0 and zero
+ *   codes.  (Scale per block and head, not per layer as the FP8 paragraph of
+ *   froggydisk's page suggests.)  The entries of one call that fill
+ *   consecutive rows r0, r0+1, ... of a block (consecutive entries slot,
+ *   slot+1, ...) form a run:
+ *     - r0 = 0 (a prompt, or the first token of a fresh block): scale =
+ *       absmax / 448 over the run's rows (fp32, IEEE division);
+ *     - r0 > 0 (appending, e.g. one decode token): rows 0 .. r0-1 must hold
+ *       codes written earlier; the scale becomes absmax / 448 over those rows
+ *       as they read back (code value x old scale, fp32) and the new rows;
+ *       the old codes are re-encoded from their read-back values only if the
+ *       scale changed.
+ *   Within one call a block may receive at most one run; two runs into one
+ *   block in the same call race (undefined result).
  *   Rows of a block past the last one written keep whatever they held and are
  *   never read as long as the context lengths exclude them. */
 kvd_status kvd_write_kv(const kvd_pool* pool, int32_t layer, const void* k, const void* v,
@@ -206,6 +213,12 @@ kvd_status kvd_merge_partials(const float* part_o, const float* part_lse, int32_
 
 /* Static string naming a status. */
 const char* kvd_status_string(kvd_status status);
+
+/* Name and description of the HIP error behind the calling thread's most
+ * recent KVD_ERR_HIP (like errno: per thread, kept until the next such error;
+ * "hipSuccess: ..." if there was none).  The string is owned by the library
+ * and valid until the thread's next call of this function. */
+const char* kvd_last_hip_error(void);
 
 /* ---- test hooks: expose device-side pieces of the hot path ------------- */
 
