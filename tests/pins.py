@@ -441,3 +441,116 @@ def fp8_append_failures(seed=9) -> list:
     if gs[0, 0] != 1.0 or gs2[0, 0] != 2.0 or not np.array_equal(back, np.concatenate([g, g2]).astype(np.float64)):
         bad.append("grid")
     return bad
+
+
+# ---------------------------------------------------------------- block manager
+def _blocks_invariant_failures(bp) -> list:
+    """Every block is free, evictable or referenced, exactly once; a block's count
+    is the number of live tables holding it; each table has ceil(len/16) blocks."""
+    bad = []
+    count = [0] * bp.num_blocks
+    for sid, seq in bp.seqs.items():
+        if len(seq["blocks"]) != -(-seq["len"] // 16):
+            bad.append(("waste", sid))
+        for b in seq["blocks"]:
+            count[b] += 1
+    if count != bp.ref:
+        bad.append("refcount")
+    free, evict = set(bp.free), set(bp.evictable)
+    used = {b for b in range(bp.num_blocks) if bp.ref[b] > 0}
+    if free & evict or free & used or evict & used or len(free | evict | used) != bp.num_blocks:
+        bad.append("partition")
+    if len(free) != len(bp.free) or len(evict) != len(bp.evictable):
+        bad.append("duplicates")
+    return bad
+
+
+def block_manager_failures(seed=12) -> list:
+    from oracle import blocks
+    bad = []
+    g = _golden("block_table_example.json")
+    # the page's three tables: the requests grow in turn, lowest free block first
+    bp = blocks.BlockPool(g["pool_blocks"])
+    a, _ = bp.add_sequence(16)
+    b, _ = bp.add_sequence(32)
+    c, _ = bp.add_sequence(16)
+    for sid, n in [(a, 16), (b, 32), (c, 16), (b, 32), (c, 16)]:
+        bp.append(sid, n)
+    got = {"A": bp.table(a), "B": bp.table(b), "C": bp.table(c)}
+    if got != g["tables"]:
+        bad.append(("example", got))
+    for name, sid in [("A", a), ("B", b), ("C", c)]:
+        if bp.slots(sid, 0, bp.length(sid)) != [paged.slot(g["tables"][name], t) for t in range(bp.length(sid))]:
+            bad.append(("slots", name))
+    bad += _blocks_invariant_failures(bp)
+    # random traffic without prefix caching: no block is ever shared, waste <= 15
+    rng = np.random.default_rng(seed)
+    bp = blocks.BlockPool(40)
+    live = []
+    for _ in range(400):
+        op = rng.integers(3)
+        try:
+            if op == 0 or not live:
+                live.append(bp.add_sequence(int(rng.integers(0, 60)))[0])
+            elif op == 1:
+                bp.append(live[int(rng.integers(len(live)))], int(rng.integers(1, 20)))
+            else:
+                bp.free_sequence(live.pop(int(rng.integers(len(live)))))
+        except blocks.NoBlocks:
+            pass
+        inv = _blocks_invariant_failures(bp)
+        if inv:
+            bad.append(("random", inv))
+            break
+        if max(bp.ref) > 1:
+            bad.append("shared_without_prefix_cache")
+            break
+    # prefix cache
+    T = [int(x) for x in rng.integers(0, 1000, 40)]
+    bp = blocks.BlockPool(12, prefix_cache=True)
+    p, n0 = bp.add_sequence(40, T)
+    q, n1 = bp.add_sequence(40, T)
+    if n0 != 0 or n1 != 32 or bp.table(q)[:2] != bp.table(p)[:2] or bp.table(q)[2] == bp.table(p)[2]:
+        bad.append(("reuse", n0, n1))          # two full blocks reused; the 8-token tail never
+    if [bp.ref[x] for x in bp.table(p)] != [2, 2, 1]:
+        bad.append("reuse_counts")
+    T1 = list(T)
+    T1[0] += 1                                  # a different first token: nothing matches
+    r, n2 = bp.add_sequence(40, T1)
+    T2 = list(T)
+    T2[20] += 1                                 # a difference in block 1: block 0 only
+    s_, n3 = bp.add_sequence(40, T2)
+    if n2 != 0 or n3 != 16:
+        bad.append(("first_miss", n2, n3))
+    bad += _blocks_invariant_failures(bp)
+    # a block that fills during decoding becomes reusable too
+    bp.append(p, 8, [7] * 8)
+    t_, n4 = bp.add_sequence(48, T + [7] * 8)
+    if n4 != 48:
+        bad.append(("decode_filled", n4))
+    # eviction: only unreferenced blocks, least recently released first
+    bp = blocks.BlockPool(4, prefix_cache=True)
+    p, _ = bp.add_sequence(32, T[:32])          # blocks 0, 1
+    q, _ = bp.add_sequence(16, T[:16])          # shares block 0
+    bp.free_sequence(p)                         # block 1 evictable; block 0 still held by q
+    x, _ = bp.add_sequence(32)                  # free blocks 2, 3
+    y, _ = bp.add_sequence(16)                  # must evict block 1, never block 0
+    if bp.table(y) != [1] or bp.ref[0] != 1:
+        bad.append(("evict", bp.table(y)))
+    before = (list(bp.free), list(bp.evictable), list(bp.ref), {k: list(v["blocks"]) for k, v in bp.seqs.items()})
+    try:
+        bp.add_sequence(16)                     # nothing left: fails and changes nothing
+        bad.append("no_fail")
+    except blocks.NoBlocks:
+        pass
+    after = (list(bp.free), list(bp.evictable), list(bp.ref), {k: list(v["blocks"]) for k, v in bp.seqs.items()})
+    if before != after:
+        bad.append("atomic")
+    # release order: the tail of a finished request is evicted before its head
+    bp = blocks.BlockPool(3, prefix_cache=True)
+    p, _ = bp.add_sequence(48, T[:32] + [1] * 16)
+    bp.free_sequence(p)
+    z, _ = bp.add_sequence(16)
+    if bp.table(z) != [2]:
+        bad.append(("release_order", bp.table(z)))
+    return bad

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import pins
-from oracle import attention, e4m3, footprint, paged, scores
+from oracle import attention, blocks, e4m3, footprint, paged, scores
 
 
 def _all_pins_pass() -> bool:
@@ -28,7 +28,8 @@ def _all_pins_pass() -> bool:
             and pins.placement_invariance_max_error() == 0.0
             and pins.score_failures() == []
             and pins.fp8_quant_failures() == []
-            and pins.fp8_append_failures() == [])
+            and pins.fp8_append_failures() == []
+            and pins.block_manager_failures() == [])
 
 
 def _modulo_heads(h, n_q, n_kv):
@@ -143,6 +144,43 @@ def _append_new_rows_old_scale(codes, scale, x_new):
     return np.concatenate([codes, e4m3.quantize_tile(x_new, enc_scale)]), ns
 
 
+def _take_highest_first(self):
+    if self.free:
+        b = max(self.free)
+        self.free.remove(b)
+    else:
+        b = self.evictable.pop(0)
+        del self.cache[self.key_of.pop(b)]
+    self.ref[b] = 1
+    return b
+
+
+def _take_most_recent(self):
+    if self.free:
+        b = min(self.free)
+        self.free.remove(b)
+    else:
+        b = self.evictable.pop()
+        del self.cache[self.key_of.pop(b)]
+    self.ref[b] = 1
+    return b
+
+
+def _release_to_free_list(self, b):
+    self.ref[b] -= 1
+    if self.ref[b] == 0:
+        self.free.append(b)
+
+
+def _release_ignoring_holders(self, b):
+    self.ref[b] = 0
+    if b in self.key_of:
+        if b not in self.evictable:
+            self.evictable.append(b)
+    elif b not in self.free:
+        self.free.append(b)
+
+
 MUTATIONS = [
     ("heads modulo instead of grouped", attention, "head_group", _modulo_heads),
     ("logit scale dropped", attention, "logits", _no_scale_logits),
@@ -160,6 +198,10 @@ MUTATIONS = [
     ("fp8 append absmax of new rows only", e4m3, "append_tile", _append_absmax_new_rows_only),
     ("fp8 append keeps stale codes", e4m3, "append_tile", _append_never_reencodes),
     ("fp8 append encodes new rows with old scale", e4m3, "append_tile", _append_new_rows_old_scale),
+    ("blocks handed out highest first", blocks.BlockPool, "_take", _take_highest_first),
+    ("evicts the most recently released", blocks.BlockPool, "_take", _take_most_recent),
+    ("finished blocks not kept for reuse", blocks.BlockPool, "_release", _release_to_free_list),
+    ("release ignores other holders", blocks.BlockPool, "_release", _release_ignoring_holders),
 ]
 
 

@@ -117,6 +117,10 @@ def test_fp8_append_requantise():
     assert pins.fp8_append_failures() == []
 
 
+def test_block_manager():
+    assert pins.block_manager_failures() == []
+
+
 @pytest.mark.parametrize("g", [1, 2, 4, 8])
 @pytest.mark.parametrize("d", [64, 128])
 def test_brute_force_grid(g, d):
