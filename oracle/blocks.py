@@ -27,8 +27,9 @@ Readings taken where the page leaves a choice open:
 * the lookup key is the whole token prefix up to and including the block (the
   exact content the page's hash stands for, so no two different prefixes can
   collide);
-* a block is registered in the prefix cache when it becomes full, unless the
-  same prefix is registered already (then it stays private);
+* a block is registered in the prefix cache at the moment it becomes full (a
+  prompt's full blocks when the request arrives), unless the same prefix is
+  registered already -- then it stays private for good;
 * blocks never registered go straight back to the free list at count 0;
   registered ones become evictable and are evicted least recently released
   first, and only when no free block is left; a finished request releases
@@ -79,16 +80,16 @@ class BlockPool:
             else:
                 self.free.append(b)
 
-    def _register_full_blocks(self, seq):
+    def _register(self, seq, k: int):
+        """Block k of ``seq`` has just become full: record it under its prefix."""
         toks = seq["tokens"]
         if not self.prefix_cache or toks is None:
             return
-        for k in range(seq["len"] // BLOCK):
-            b = seq["blocks"][k]
-            key = tuple(toks[:BLOCK * (k + 1)])
-            if key not in self.cache and b not in self.key_of:
-                self.cache[key] = b
-                self.key_of[b] = key
+        b = seq["blocks"][k]
+        key = tuple(toks[:BLOCK * (k + 1)])
+        if key not in self.cache and b not in self.key_of:
+            self.cache[key] = b
+            self.key_of[b] = key
 
     # ------------------------------------------------------------ calls
     def add_sequence(self, n: int, tokens=None):
@@ -113,7 +114,8 @@ class BlockPool:
         sid = self.next_id
         self.next_id += 1
         self.seqs[sid] = {"blocks": blocks, "len": n, "tokens": toks}
-        self._register_full_blocks(self.seqs[sid])
+        for k in range(n // BLOCK):
+            self._register(self.seqs[sid], k)
         return sid, BLOCK * len(found)
 
     def append(self, sid: int, n: int = 1, tokens=None):
@@ -129,7 +131,8 @@ class BlockPool:
         if seq["tokens"] is not None:
             # without the new tokens' ids the content is unknown: stop registering
             seq["tokens"] = seq["tokens"] + list(tokens) if tokens is not None else None
-        self._register_full_blocks(seq)
+        for k in range(old // BLOCK, (old + n) // BLOCK):
+            self._register(seq, k)
         return self.slots(sid, old, n)
 
     def slots(self, sid: int, first: int, n: int):
