@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libkvdecode.so")
 BLOCK_SIZE = 16
 KVD_BF16, KVD_FP8_E4M3 = 0, 1
 STATUS = {0: "KVD_OK", 1: "KVD_ERR_INVALID_ARG", 2: "KVD_ERR_UNSUPPORTED", 3: "KVD_ERR_DTYPE",
-          4: "KVD_ERR_WORKSPACE", 5: "KVD_ERR_HIP"}
+          4: "KVD_ERR_WORKSPACE", 5: "KVD_ERR_HIP", 6: "KVD_ERR_CAPACITY"}
+KVD_ERR_CAPACITY = 6
 
 
 class KvdError(RuntimeError):
@@ -65,6 +66,22 @@ EXPORTS = {
                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p),
     "kvd_debug_fp8_decode": (ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p),
+    # host block bookkeeping (kvblocks.h)
+    "kvd_bm_create": (ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)),
+    "kvd_bm_destroy": (ctypes.c_void_p,),
+    "kvd_bm_add_sequence": (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                            ctypes.POINTER(ctypes.c_int32)),
+    "kvd_bm_append": (ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p),
+    "kvd_bm_slots": (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p),
+    "kvd_bm_length": (ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)),
+    "kvd_bm_block_table": (ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                           ctypes.POINTER(ctypes.c_int32)),
+    "kvd_bm_fill_tables": (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                           ctypes.c_void_p),
+    "kvd_bm_free_sequence": (ctypes.c_void_p, ctypes.c_int64),
+    "kvd_bm_counts": (ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                      ctypes.POINTER(ctypes.c_int32)),
+    "kvd_bm_refcount": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)),
 }
 
 
@@ -334,3 +351,97 @@ def decode(pool: Pool, layer: int, q, block_table, context_lens, max_context_len
         ws = allocate_workspace(pool, args, device=q.device)
     (kvd_decode_attn_fp8 if pool.fp8 else kvd_decode_attn)(pool, layer, args, stream)
     return out, ws
+
+
+# ---------------------------------------------------------------- block bookkeeping
+def _i32(values):
+    """Host int32 array (numpy) and its address."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(values, dtype=np.int32))
+    return a, a.ctypes.data
+
+
+class BlockManager:
+    """Host block bookkeeping of a paged pool (kvblocks.h): free list, reference
+    counts, on-demand growth and, optionally, the prefix cache.  Marshalling
+    only; every decision is made by the native library."""
+
+    def __init__(self, num_blocks: int, prefix_cache: bool = False):
+        h = ctypes.c_void_p()
+        _check(lib.kvd_bm_create(int(num_blocks), 1 if prefix_cache else 0, ctypes.byref(h)), "kvd_bm_create")
+        self.handle = h.value
+        self.num_blocks = int(num_blocks)
+
+    def __del__(self):
+        if getattr(self, "handle", None) and lib is not None:
+            lib.kvd_bm_destroy(self.handle)
+            self.handle = None
+
+    def add_sequence(self, n_tokens: int, tokens=None):
+        """Returns (sequence id, number of leading prompt tokens already cached)."""
+        sid, cached = ctypes.c_int64(), ctypes.c_int32()
+        if tokens is not None:
+            arr, ptr = _i32(tokens)
+            _require(arr.shape == (n_tokens,), "tokens must hold n_tokens ids")
+        else:
+            arr, ptr = None, None
+        _check(lib.kvd_bm_add_sequence(self.handle, ptr, int(n_tokens), ctypes.byref(sid), ctypes.byref(cached)),
+               "kvd_bm_add_sequence")
+        return sid.value, cached.value
+
+    def append(self, seq_id: int, n: int = 1, tokens=None):
+        """Append n tokens; returns their slots (the slot mapping of kvd_write_kv)."""
+        import numpy as np
+        slots = np.zeros(max(n, 1), dtype=np.int32)
+        if tokens is not None:
+            arr, ptr = _i32(tokens)
+            _require(arr.shape == (n,), "tokens must hold n ids")
+        else:
+            arr, ptr = None, None
+        _check(lib.kvd_bm_append(self.handle, int(seq_id), ptr, int(n), slots.ctypes.data), "kvd_bm_append")
+        return [int(x) for x in slots[:n]]
+
+    def slots(self, seq_id: int, first: int, n: int):
+        import numpy as np
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        _check(lib.kvd_bm_slots(self.handle, int(seq_id), int(first), int(n), out.ctypes.data), "kvd_bm_slots")
+        return [int(x) for x in out[:n]]
+
+    def length(self, seq_id: int) -> int:
+        n = ctypes.c_int32()
+        _check(lib.kvd_bm_length(self.handle, int(seq_id), ctypes.byref(n)), "kvd_bm_length")
+        return n.value
+
+    def table(self, seq_id: int):
+        import numpy as np
+        n = ctypes.c_int32()
+        cap = -(-self.length(seq_id) // BLOCK_SIZE)
+        out = np.zeros(max(cap, 1), dtype=np.int32)
+        _check(lib.kvd_bm_block_table(self.handle, int(seq_id), out.ctypes.data, cap, ctypes.byref(n)),
+               "kvd_bm_block_table")
+        return [int(x) for x in out[:n.value]]
+
+    def fill_tables(self, seq_ids, max_blocks: int):
+        """(block table int32 [b][max_blocks] padded with -1, context lengths int32 [b]) as numpy."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        b = int(ids.shape[0])
+        table = np.full((max(b, 1), max_blocks), -1, dtype=np.int32)
+        lens = np.zeros(max(b, 1), dtype=np.int32)
+        _check(lib.kvd_bm_fill_tables(self.handle, ids.ctypes.data, b, table.ctypes.data, int(max_blocks),
+                                      lens.ctypes.data), "kvd_bm_fill_tables")
+        return table[:b], lens[:b]
+
+    def free_sequence(self, seq_id: int):
+        _check(lib.kvd_bm_free_sequence(self.handle, int(seq_id)), "kvd_bm_free_sequence")
+
+    def counts(self):
+        """(free, cached but unused, used) block counts."""
+        f, c, u = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib.kvd_bm_counts(self.handle, ctypes.byref(f), ctypes.byref(c), ctypes.byref(u)), "kvd_bm_counts")
+        return f.value, c.value, u.value
+
+    def refcount(self, block: int) -> int:
+        r = ctypes.c_int32()
+        _check(lib.kvd_bm_refcount(self.handle, int(block), ctypes.byref(r)), "kvd_bm_refcount")
+        return r.value

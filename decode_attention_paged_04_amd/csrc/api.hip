@@ -305,6 +305,7 @@ const char* kvd_status_string(kvd_status s) {
     case KVD_ERR_DTYPE: return "KVD_ERR_DTYPE";
     case KVD_ERR_WORKSPACE: return "KVD_ERR_WORKSPACE";
     case KVD_ERR_HIP: return "KVD_ERR_HIP";
+    case KVD_ERR_CAPACITY: return "KVD_ERR_CAPACITY";
   }
   return "KVD_ERR_UNKNOWN";
 }

@@ -47,7 +47,8 @@ typedef enum {
   KVD_ERR_UNSUPPORTED = 2,  /* valid but not built: d_h, block size, sizes   */
   KVD_ERR_DTYPE = 3,        /* bf16 entry point on an FP8 pool or vice versa */
   KVD_ERR_WORKSPACE = 4,    /* workspace missing or too small                */
-  KVD_ERR_HIP = 5           /* a HIP launch or query failed                  */
+  KVD_ERR_HIP = 5,          /* a HIP launch or query failed                  */
+  KVD_ERR_CAPACITY = 6      /* not enough free blocks (or host memory)       */
 } kvd_status;
 
 /* KV element type of a pool.

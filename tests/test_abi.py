@@ -18,7 +18,8 @@ FAKE = 1 << 24            # 16-byte aligned stand-in for a device pointer
 
 
 def header_symbols():
-    hdr = open(os.path.join(ROOT, "include", "kvdecode.h")).read()
+    inc = os.path.join(ROOT, "include")
+    hdr = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
     return sorted(set(re.findall(r"\b(kvd_[a-z0-9_]+)\s*\(", hdr)))
 
