@@ -28,6 +28,8 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+
+import numpy as np
 import hashlib
 import json
 import math
@@ -72,13 +74,13 @@ def algorithmic_step_bytes(lens, layers, n_q, n_kv, head_dim, kv_bytes, fp8, sco
 class Workload:
     """A workload resident in HBM, ready to be stepped (eagerly or from graphs)."""
 
-    def __init__(self, name: str, chunk: int, replicas: int):
+    def __init__(self, name: str, chunk: int, replicas: int, layers: int = 0):
         import torch
         import decode_attention_paged_04_amd as kvd
         import workloads as W
 
         self.kvd, self.torch = kvd, torch
-        self.w = w = W.WORKLOADS[name]
+        self.w = w = W.WORKLOADS[name] if not layers else W.WORKLOADS[name].with_(layers=layers)
         self.fp8 = w.kv_dtype == "fp8"
         self.lens = W.context_lengths(w)
         self.table, self.num_blocks = W.block_tables(w, self.lens)
@@ -96,6 +98,11 @@ class Workload:
         self.table_t = torch.from_numpy(self.table).to(dev)
         slots = kvd.slot_mapping_for(self.table_t, self.lens_t)
         n_tok = int(self.lens.sum())
+        offs = W.offsets(self.lens)
+        for i in range(1, w.b):                 # a shared prefix is stored once, by sequence 0
+            slots[int(offs[i]):int(offs[i]) + w.shared_prefix] = -1
+        self.unique_step_bytes = self.step_bytes - w.layers * (w.b - 1) * w.shared_prefix * (
+            2 * w.n_kv * w.head_dim * self.kv_bytes)
         dt = kvd.KVD_FP8_E4M3 if self.fp8 else kvd.KVD_BF16
         t0 = time.time()
         self.pools = [kvd.allocate_pool(w.layers, self.num_blocks, w.n_kv, w.head_dim, dt)
@@ -206,13 +213,35 @@ class Workload:
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n / 1e3
 
+    def time_append(self, n: int) -> float:
+        """Mean duration (s) of one kvd_write_kv call storing one token per
+        sequence -- what a decode step writes per layer -- into each
+        sequence's last block (a partly filled block re-quantises under FP8)."""
+        torch, kvd, w = self.torch, self.kvd, self.w
+        last = torch.from_numpy(self.table[np.arange(w.b), (self.lens - 1) // 16] * 16 + (self.lens - 1) % 16)
+        slots = last.to(torch.int32).cuda()
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.seed)
+        K = torch.randn((w.b, w.n_kv, w.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+        V = torch.randn((w.b, w.n_kv, w.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+        stream = torch.cuda.current_stream()
+        for k in range(4):
+            kvd.kvd_write_kv(self.pools[0], k % w.layers, K, V, slots)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for k in range(n):
+            kvd.kvd_write_kv(self.pools[0], k % w.layers, K, V, slots)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n / 1e3
+
     def config(self):
         w = self.w
         ctx = (str(int(w.ctx[1])) if w.ctx[0] == "fixed"
                else f"U[{w.ctx[1]},{w.ctx[2]}] (sum {int(self.lens.sum())})")
         return {"workload": w.name, "b": w.b, "layers": w.layers, "n_q": w.n_q, "n_kv": w.n_kv,
                 "head_dim": w.head_dim, "context": ctx, "block_size": 16,
-                "kv_dtype": w.kv_dtype, "fused_scores": bool(w.scores),
+                "kv_dtype": w.kv_dtype, "fused_scores": bool(w.scores), "shared_prefix": w.shared_prefix,
                 "chunk_tokens": self.chunk, "n_chunks": self.n_chunks, "pool_replicas": self.R,
                 "num_blocks": self.num_blocks, "hip_graphs": True}
 
@@ -302,6 +331,36 @@ def measure(name: str, chunk: int, replicas: int, steps: int, warmup: int, launc
     return wl, res
 
 
+def extra_entry(name: str, steps: int):
+    """A further workload in the same line: step rate, kernel roofline, and for a
+    shared prefix the rate over the bytes actually stored (each shared block once)."""
+    wl, r = measure(name, 0, 0, steps, 2, 40)
+    e = {"workload": r["config"]["workload"], "value": round(r["value"], 2), "unit": "GB/s",
+         "ms_per_step": round(r["ms_per_step"], 4), "steps": steps,
+         "seq_steps_per_s": round(r["seq_steps_per_s"], 3), "pct_of_hbm_peak": round(r["pct_of_hbm_peak"], 2),
+         "config": r["config"],
+         "roofline": {"bound": "hbm", "achieved": round(r["achieved"], 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": round(r["achieved"] / PEAK_HBM_GBS, 4), "traffic": measured_traffic(name),
+                      "launch_us": round(r["launch_us"], 2)}}
+    if wl.w.shared_prefix:
+        e["unique_bytes_per_step"] = wl.unique_step_bytes
+        e["unique_GBs"] = round(wl.unique_step_bytes / (r["ms_per_step"] / 1e3) / 1e9, 1)
+    wl.free()
+    return e
+
+
+def append_entry(name: str, calls: int):
+    """Cost of the decode step's own write: one token per sequence per layer."""
+    wl = Workload(name, 0, 1, layers=1)
+    s = wl.time_append(calls)
+    w = wl.w
+    e = {"workload": f"{w.name} (1 layer)", "kv_dtype": w.kv_dtype, "tokens_per_call": w.b,
+         "us_per_call": round(s * 1e6, 2),
+         "stored_bytes_per_call": w.b * 2 * w.n_kv * w.head_dim * wl.kv_bytes}
+    wl.free()
+    return e
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,6 +372,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="chunk_tokens (0 = the library's choice)")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas (0 = enough to exceed the cache)")
     ap.add_argument("--launches", type=int, default=200, help="event-timed launches for the roofline")
+    ap.add_argument("--extras", default="70b_shard,8b_prefix",
+                    help="further workloads reported in the same line (comma list), or 'none'")
+    ap.add_argument("--no-append", action="store_true", help="skip the append-cost entries")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -368,6 +430,15 @@ def main():
                                   "frac": round(sec["achieved"] / PEAK_HBM_GBS, 4),
                                   "traffic": traffic2, "launch_us": round(sec["launch_us"], 2)}}
 
+    extras = []
+    if args.extras != "none":
+        for name in args.extras.split(","):
+            extras.append(extra_entry(name, 10))
+    appends = []
+    if not args.no_append:
+        for name in ("8b_ragged", "8b_fp8_scores"):
+            appends.append(append_entry(name, 200))
+
     traffic = measured_traffic(args.workload)
     line = {
         "metric": METRIC,
@@ -391,6 +462,8 @@ def main():
                      "bytes_per_launch": head["launch_bytes"]},
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "extra": extras,
+        "append": appends,
     }
     print(json.dumps(line), flush=True)
 

@@ -45,6 +45,7 @@ class DecodeWorkload:
     kv_dtype: str = "bf16"      # "bf16" or "fp8"
     channel_scale: bool = False  # per-(kv-head, channel) magnitudes ~ U[0.5, 2]
     scores: bool = False        # fused cumulative score output requested
+    shared_prefix: int = 0      # leading tokens whose blocks every sequence shares (multiple of 16)
 
     @property
     def g(self) -> int:
@@ -66,6 +67,13 @@ WORKLOADS = {
                                 ctx=("uniform", 4096, 16384)),
     "70b_long": DecodeWorkload("llama3-70b-80layer-b4-s131072", seed=4, b=4, layers=80,
                                n_q=64, n_kv=8, head_dim=128, ctx=("fixed", 131072)),
+    # one GPU's share of the 70B request when its context is split over 8 GPUs
+    "70b_shard": DecodeWorkload("llama3-70b-80layer-b4-s16384-context-shard-of-8", seed=6, b=4,
+                                layers=80, n_q=64, n_kv=8, head_dim=128, ctx=("fixed", 16384)),
+    # 32 requests behind one 16,384-token system prompt whose blocks they all share
+    "8b_prefix": DecodeWorkload("llama3.1-8b-8layer-b32-shared16k+1k", seed=7, b=32, layers=8,
+                                n_q=32, n_kv=8, head_dim=128, ctx=("fixed", 17408),
+                                shared_prefix=16384),
     "8b_fp8_scores": DecodeWorkload("llama3.1-8b-fp8-scores-32layer-b32-s8k..32k", seed=5,
                                     b=32, layers=32, n_q=32, n_kv=8, head_dim=128,
                                     ctx=("uniform", 8192, 32768), kv_dtype="fp8",
@@ -96,17 +104,21 @@ def block_tables(w: DecodeWorkload, lens: np.ndarray,
     """
     rng = rng or np.random.default_rng(w.seed + 1000)
     need = [cdiv(int(s), BLOCK_SIZE) for s in lens]
-    total = sum(need)
+    shared = w.shared_prefix // BLOCK_SIZE
+    if w.shared_prefix % BLOCK_SIZE or any(n < shared for n in need):
+        raise ValueError("the shared prefix must be whole blocks inside every sequence")
+    total = shared + sum(n - shared for n in need)
     num_blocks = w.pool_blocks if w.pool_blocks is not None else total
     if num_blocks < total:
         raise ValueError(f"pool of {num_blocks} blocks cannot hold {total}")
     perm = rng.permutation(num_blocks).astype(np.int32)
     max_blocks = max(max(need, default=0), 1)
     table = np.full((len(need), max_blocks), pad_value, dtype=np.int32)
-    cur = 0
+    cur = shared
     for i, n in enumerate(need):
-        table[i, :n] = perm[cur:cur + n]
-        cur += n
+        table[i, :shared] = perm[:shared]
+        table[i, shared:n] = perm[cur:cur + n - shared]
+        cur += n - shared
     return table, num_blocks
 
 
