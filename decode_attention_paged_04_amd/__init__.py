@@ -86,6 +86,13 @@ EXPORTS = {
 
 
 def _load():
+    # PyTorch's ROCm build carries its own HIP runtime (libamdhip64.so, same
+    # soname as the system's).  Importing torch first makes the library's
+    # libamdhip64.so.7 dependency resolve to that already-loaded runtime, so
+    # the process holds one HIP runtime; loading the library first would map a
+    # second one beside torch's, and the second runtime to touch the device can
+    # fail with hipErrorNoDevice.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m decode_attention_paged_04_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
