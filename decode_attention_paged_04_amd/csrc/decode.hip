@@ -128,15 +128,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeLaunch a) 
     const int32_t pid1 = live && nvalid > kBlock ? load_invariant(bt + 2 * p + 1) : -1;
     const uint32_t t0 = tile_pair_offset(pid0, j, a.num_blocks, a.n_kv, TPB);
     const uint32_t t1 = tile_pair_offset(pid1, j, a.num_blocks, a.n_kv, TPB);
-    // K: S-tile t, row r16 -> block r16/8, in-block row 8*((r16/4)&1) + 4t + r16%4;
-    // this lane's 16-byte units sit at byte 64u + 16G of that row.
+    // K: S-tile t, row r16 -> block r16/8, in-block row 8*((r16/4)&1) + 4t + r16%4,
+    // whose 16-byte unit u for lane group G (piece 4u + G of the row) is K piece
+    // ((t*KU + u)*4 + G)*8 + r16%8 of the block: each load reads 512 contiguous
+    // bytes per block.
     const uint32_t tk = r16 < 8 ? t0 : t1;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int row = 8 * ((r16 >> 2) & 1) + 4 * t + (r16 & 3);
 #pragma unroll
       for (int u = 0; u < R::KU; ++u) {
-        const uint32_t off = tk + (uint32_t)(row * D * E + 64 * u + 16 * G);
+        const uint32_t off = tk + (uint32_t)((((t * R::KU + u) * 4 + G) * 8 + (r16 & 7)) * 16);
         f.k[t][u] = load16(rs, tk == kOutOfRange ? kOutOfRange : off);
       }
     }

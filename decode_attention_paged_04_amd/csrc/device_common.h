@@ -57,9 +57,18 @@ __host__ __device__ inline uint32_t tile_pair_offset(int32_t p, int32_t j, int32
   return ((uint32_t)p * (uint32_t)n_kv + (uint32_t)j) * tile_pair_bytes;
 }
 
-// Element offsets inside a tile pair: K token-major, V channel-major.
-__host__ __device__ inline uint32_t k_elem(int row, int ch, int head_dim) {
-  return (uint32_t)(row * head_dim + ch);
+// Element offsets inside a tile pair (w = elem_bytes, n = 16 / w elements per
+// 16 bytes, P = head_dim / n pieces per row).  The K tile is stored as 16-byte
+// pieces in the operand order of the decode kernels' q.K^T MFMA: piece
+// (s * P + q) * 8 + r holds channels q n .. q n + n - 1 of in-block row
+// 8 (r / 4) + 4 s + r % 4, so the 32 lanes that read one block in one load
+// instruction read 512 contiguous bytes.  The V tile is channel-major: 16
+// consecutive rows of each channel.
+__host__ __device__ inline uint32_t k_elem(int row, int ch, int head_dim, int elem_bytes) {
+  const int n = 16 / elem_bytes;
+  const int s = (row >> 2) & 1;
+  const int r = ((row >> 3) << 2) | (row & 3);
+  return (uint32_t)(((s * (head_dim / n) + ch / n) * 8 + r) * n + ch % n);
 }
 __host__ __device__ inline uint32_t v_elem(int row, int ch, int head_dim) {
   return (uint32_t)(16 * head_dim + ch * 16 + row);

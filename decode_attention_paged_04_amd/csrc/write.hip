@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void write_bf16_kernel(char* __restrict__ laye
   const int row = slot % kBlock;
   if (p >= num_blocks) return;
   uint16_t* tile = reinterpret_cast<uint16_t*>(layer_base + ((size_t)p * n_kv + j) * (2 * kBlock * D * 2));
-  tile[k_elem(row, ch, D)] = k[e];
+  tile[k_elem(row, ch, D, 2)] = k[e];
   tile[v_elem(row, ch, D)] = v[e];
 }
 
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(64) void write_fp8_kernel(char* __restrict__ layer_
   const size_t row_stride = (size_t)n_kv * D;
   uint8_t* tile = reinterpret_cast<uint8_t*>(layer_base + ((size_t)p * n_kv + j) * (2 * kBlock * D));
   float* scale_at = layer_scales + ((size_t)p * n_kv + j) * 2 + which;
-  auto at = [&](int r, int ch) -> uint8_t& { return tile[which ? v_elem(r, ch, D) : k_elem(r, ch, D)]; };
+  auto at = [&](int r, int ch) -> uint8_t& { return tile[which ? v_elem(r, ch, D) : k_elem(r, ch, D, 1)]; };
 
   const float s_old = r0 > 0 ? *scale_at : 0.f;
   float am = 0.f;
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void debug_offsets_kernel(int64_t layer_elem0,
     return;
   }
   const int64_t tile_elem = layer_elem0 + (int64_t)(off / (uint32_t)elem_bytes);
-  out_k[e] = tile_elem + k_elem(t % kBlock, 0, head_dim);
+  out_k[e] = tile_elem + k_elem(t % kBlock, 0, head_dim, elem_bytes);
   out_v[e] = tile_elem + v_elem(t % kBlock, 0, head_dim);
 }
 

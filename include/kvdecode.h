@@ -72,11 +72,14 @@ typedef struct {
  *
  *   tile pair of (layer l, physical block p, KV head j) starts at element
  *       T = ((l * num_blocks + p) * n_kv + j) * (2 * 16 * head_dim)
- *   K of in-block row t (0..15), channel c:  T + t * head_dim + c
+ *   K of in-block row t (0..15), channel c, with n = 16 / w elements per 16
+ *   bytes, P = head_dim / n, s = (t / 4) % 2, r = 4 (t / 8) + t % 4:
+ *       T + ((s * P + c / n) * 8 + r) * n + c % n
  *   V of in-block row t,         channel c:  T + 16 * head_dim + c * 16 + t
  *
  * so one (block, head) is one contiguous 2*16*head_dim*w-byte region: the K
- * tile token-major, then the V tile channel-major.  Logical token t of a
+ * tile as 16-byte pieces in the decode kernel's MFMA operand order (each
+ * piece n channels of one row), then the V tile channel-major.  Logical token t of a
  * sequence lives in physical block table[t / 16] at in-block row t % 16.
  * FP8 pools add fp32 scales, one per (layer, block, KV head) for K and one
  * for V, at scale_base[((l * num_blocks + p) * n_kv + j) * 2 + {0: K, 1: V}];

@@ -14,10 +14,15 @@ of the library's code:
 
 * element offset of the tile pair of (layer l, physical block p, KV head j):
   ``((l * num_blocks + p) * n_kv + j) * 2 * 16 * head_dim``
-* K of in-block row t, channel c: ``+ t * head_dim + c``          (token-major)
+* K is kept as 16-byte pieces of n = 16 / w channels (w the element size,
+  P = head_dim / n pieces per row); row t's channel c lies in piece q = c // n
+  of the row, and with s = (t // 4) % 2 and r = 4 (t // 8) + t % 4 that
+  piece is piece number (s P + q) 8 + r of the tile, channel c sitting at
+  position c % n inside it;
 * V of in-block row t, channel c: ``+ 16 * head_dim + c * 16 + t`` (channel-major)
-* FP8 pools use the same offsets in bytes; the fp32 scale of (l, p, j) is at
-  index ``((l * num_blocks + p) * n_kv + j) * 2`` (+0 for K, +1 for V).
+* FP8 pools use the same rules with w = 1 (offsets in bytes); the fp32 scale
+  of (l, p, j) is at index ``((l * num_blocks + p) * n_kv + j) * 2`` (+0 for
+  K, +1 for V).
 """
 from __future__ import annotations
 
@@ -52,6 +57,16 @@ class PoolLayout:
     num_blocks: int
     n_kv: int
     head_dim: int
+    elem_bytes: int = 2          # 2 for bf16 pools, 1 for FP8
+
+    def k_in_tile(self, row, ch):
+        """Element offset of K[row][ch] from the start of its tile (works on arrays)."""
+        n = 16 // self.elem_bytes
+        pieces_per_row = self.head_dim // n
+        s = (row // 4) % 2
+        r = 4 * (row // 8) + row % 4
+        piece = (s * pieces_per_row + ch // n) * 8 + r
+        return piece * n + ch % n
 
     @property
     def tile_pair_elems(self) -> int:
@@ -65,7 +80,7 @@ class PoolLayout:
         return ((layer * self.num_blocks + block) * self.n_kv + head) * self.tile_pair_elems
 
     def k_offset(self, layer: int, block: int, head: int, row: int, ch: int) -> int:
-        return self.tile_base(layer, block, head) + row * self.head_dim + ch
+        return self.tile_base(layer, block, head) + int(self.k_in_tile(row, ch))
 
     def v_offset(self, layer: int, block: int, head: int, row: int, ch: int) -> int:
         return (self.tile_base(layer, block, head) + BLOCK_SIZE * self.head_dim
@@ -111,6 +126,6 @@ def gather_indices(lay: PoolLayout, layer: int, table_row, s: int):
     heads = np.arange(lay.n_kv, dtype=np.int64)
     ch = np.arange(lay.head_dim, dtype=np.int64)
     base = ((layer * lay.num_blocks + blk)[:, None] * lay.n_kv + heads[None, :]) * lay.tile_pair_elems
-    k_idx = base[:, :, None] + row[:, None, None] * lay.head_dim + ch[None, None, :]
+    k_idx = base[:, :, None] + lay.k_in_tile(row[:, None, None], ch[None, None, :])
     v_idx = base[:, :, None] + BLOCK_SIZE * lay.head_dim + ch[None, None, :] * BLOCK_SIZE + row[:, None, None]
     return k_idx, v_idx

@@ -164,7 +164,8 @@ class PagedCase:
         return ref
 
     def layout(self):
-        return paged.PoolLayout(self.L, self.num_blocks, self.w.n_kv, self.w.head_dim)
+        return paged.PoolLayout(self.L, self.num_blocks, self.w.n_kv, self.w.head_dim,
+                                elem_bytes=1 if self.fp8 else 2)
 
 
 def score_rel_error(got: np.ndarray, ref: np.ndarray) -> float:

@@ -255,7 +255,7 @@ def block_table_example_failures() -> list:
     used = sorted(b for t in g["tables"].values() for b in t)
     if used != list(range(g["pool_blocks"])):
         bad.append("cover")
-    lay = paged.PoolLayout(num_layers=1, num_blocks=g["pool_blocks"], n_kv=2, head_dim=4)
+    lay = paged.PoolLayout(num_layers=1, num_blocks=g["pool_blocks"], n_kv=2, head_dim=8)
     pool = np.full(lay.total_elems, np.nan)
     rng = np.random.default_rng(5)
     data = {}
@@ -263,8 +263,8 @@ def block_table_example_failures() -> list:
         s = len(table) * bs - (3 if name != "A" else 0)     # the last block may be partial
         if paged.tail_waste(s) > g["max_waste_tokens"]:
             bad.append(("waste", name))
-        K = rng.standard_normal((s, 2, 4))
-        V = rng.standard_normal((s, 2, 4))
+        K = rng.standard_normal((s, 2, 8))
+        V = rng.standard_normal((s, 2, 8))
         paged.scatter(pool, lay, 0, table, K, V)
         data[name] = (table, K, V)
         # the slot of token t lies in physical block table[t // 16] at row t % 16
@@ -276,11 +276,21 @@ def block_table_example_failures() -> list:
         K2, V2 = paged.gather(pool, lay, 0, table, K.shape[0])
         if not (np.array_equal(K, K2) and np.array_equal(V, V2)):
             bad.append(("roundtrip", name))
-    # documented layout: K token-major, V channel-major inside a tile pair
-    if lay.k_offset(0, 3, 1, 2, 1) - lay.tile_base(0, 3, 1) != 2 * 4 + 1:
-        bad.append("k_layout")
-    if lay.v_offset(0, 3, 1, 2, 1) - lay.tile_base(0, 3, 1) != 16 * 4 + 1 * 16 + 2:
+    # documented layout (head_dim 8, bf16: 8 channels per 16-byte piece, one
+    # piece per row): K row t in piece 8 ((t // 4) % 2) + 4 (t // 8) + t % 4;
+    # V channel-major after the K tile; worked by hand:
+    base = lay.tile_base(0, 3, 1)
+    for row, ch, want in [(2, 1, 17), (5, 3, 75), (12, 7, 103), (15, 0, 15 * 8)]:
+        if lay.k_offset(0, 3, 1, row, ch) - base != want:
+            bad.append(("k_layout", row, ch))
+    if lay.v_offset(0, 3, 1, 2, 1) - base != 16 * 8 + 1 * 16 + 2:
         bad.append("v_layout")
+    # every K element of a tile has its own place inside the K half of the tile
+    for d, w in [(8, 2), (64, 2), (128, 2), (64, 1), (128, 1)]:
+        L2 = paged.PoolLayout(1, 1, 1, d, elem_bytes=w)
+        offs = sorted(int(L2.k_in_tile(r, c)) for r in range(16) for c in range(d))
+        if offs != list(range(16 * d)):
+            bad.append(("k_permutation", d, w))
     return bad
 
 

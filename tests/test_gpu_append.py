@@ -110,7 +110,7 @@ def test_append_matches_oracle(env, fp8, d):
     torch.cuda.synchronize()
     H.say(f"append d={d} fp8={fp8}: {len(calls)} append calls done")
 
-    lay = paged.PoolLayout(1, nb, w.n_kv, d)
+    lay = paged.PoolLayout(1, nb, w.n_kv, d, elem_bytes=1 if fp8 else 2)
     got = pool.kv.cpu().numpy()
     logical = {}
     for i, s in enumerate(FINAL):

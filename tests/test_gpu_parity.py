@@ -67,7 +67,7 @@ def test_gather_offsets_follow_the_block_table(env, dtype):
     nb, n_kv, d, L = ex["pool_blocks"], 2, 64, 3
     dt = kvd.KVD_FP8_E4M3 if dtype == "fp8" else kvd.KVD_BF16
     pool = kvd.allocate_pool(L, nb, n_kv, d, dt)
-    lay = paged.PoolLayout(L, nb, n_kv, d)
+    lay = paged.PoolLayout(L, nb, n_kv, d, elem_bytes=1 if dtype == "fp8" else 2)
     n_tok = 16 * mb
     tt = torch.from_numpy(table).cuda()
     for layer in (0, 2):
