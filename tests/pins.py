@@ -564,3 +564,80 @@ def block_manager_failures(seed=12) -> list:
     if bp.table(z) != [2]:
         bad.append(("release_order", bp.table(z)))
     return bad
+
+
+# ---------------------------------------------------------------- tiers
+def tier_failures(seed=13) -> list:
+    """Tier-restricted decode: all-kept reduces to the plain step; a brute-force
+    softmax over the kept tokens; weights 0 off the kept set and summing to 1
+    on it; the plan's protected blocks, budgets and ranking; block scores as
+    sums; the 64-step schedule; the result depends only on the evicted set."""
+    from oracle import tiers
+    rng = np.random.default_rng(seed)
+    bad = []
+    s, n_q, n_kv, d = 37, 4, 2, 8
+    q = rng.standard_normal((n_q, d))
+    K = rng.standard_normal((s, n_kv, d))
+    V = rng.standard_normal((s, n_kv, d))
+    o_all, l_all = tiers.restricted_decode(q, K, V, np.ones(s, bool))
+    o_ref, l_ref = attention.decode_sequence(q, K, V)
+    if not (np.array_equal(o_all, o_ref) and np.array_equal(l_all, l_ref)):
+        bad.append("all_kept")
+    keep = rng.random(s) < 0.5
+    keep[3] = True
+    o, lse = tiers.restricted_decode(q, K, V, keep)
+    for h in range(n_q):
+        j = h // (n_q // n_kv)
+        idx = [t for t in range(s) if keep[t]]
+        lg = [sum(q[h, c] * K[t, j, c] for c in range(d)) / math.sqrt(d) for t in idx]
+        m = max(lg)
+        e = [math.exp(x - m) for x in lg]
+        z = math.fsum(e)
+        want = [math.fsum(e[k] * V[t, j, c] for k, t in enumerate(idx)) / z for c in range(d)]
+        if np.max(np.abs(o[h] - np.array(want))) > 1e-13 or abs(lse[h] - (m + math.log(z))) > 1e-13:
+            bad.append(("brute", h))
+    a = tiers.restricted_weights(q, K, keep)
+    if np.any(a[:, ~keep] != 0) or np.max(np.abs(a[:, keep].sum(axis=1) - 1)) > 1e-12:
+        bad.append("weights")
+    o0, l0 = tiers.restricted_decode(q, K, V, np.zeros(s, bool))
+    if np.any(o0 != 0) or not np.all(np.isneginf(l0)):
+        bad.append("nothing_kept")
+    # block scores: sums over each block's tokens (the last block holds 5)
+    ts = np.arange(37, dtype=np.float64)
+    if list(tiers.block_scores(ts, 37)) != [120.0, 376.0, 170.0]:
+        bad.append("block_scores")
+    # the plan
+    sc = rng.random(20)
+    sc[7] = sc[9]                                # a tie: block 7 ranks before block 9
+    tier = tiers.plan_tiers(sc, 2, 3, 5, 4)
+    if not all(tier[b] == tiers.T0 for b in (0, 1, 17, 18, 19)):
+        bad.append("protected")
+    rest = [b for b in range(2, 17)]
+    if sum(tier[b] == tiers.T0 for b in rest) != 5 or sum(tier[b] == tiers.T1 for b in rest) != 4:
+        bad.append("budgets")
+    lo0 = min(sc[b] for b in rest if tier[b] == tiers.T0)
+    hi1, lo1 = max(sc[b] for b in rest if tier[b] == tiers.T1), min(sc[b] for b in rest if tier[b] == tiers.T1)
+    hi3 = max(sc[b] for b in rest if tier[b] == tiers.T3)
+    if not (lo0 >= hi1 and lo1 >= hi3):
+        bad.append("ranking")
+    tie = tiers.plan_tiers(np.zeros(6), 0, 0, 2, 2)
+    if list(tie) != [tiers.T0, tiers.T0, tiers.T1, tiers.T1, tiers.T3, tiers.T3]:
+        bad.append("ties")
+    if any(t == tiers.T3 for t in tiers.plan_tiers(sc, 2, 3, 10, 10)):
+        bad.append("roomy_budget")
+    if not (tiers.retier_due(0) and tiers.retier_due(128) and not tiers.retier_due(63)):
+        bad.append("delta")
+    km = tiers.kept_tokens([tiers.T0, tiers.T3, tiers.T1], 37)
+    if not (km[:16].all() and not km[16:32].any() and km[32:].all()):
+        bad.append("kept_tokens")
+    # Proposition 1: another T0/T1 split with the same evicted blocks gives the same result
+    sc3 = rng.random(3)
+    p1 = tiers.plan_tiers(sc3, 0, 1, 1, 0)
+    p2 = tiers.plan_tiers(sc3, 0, 1, 0, 1)
+    if not np.array_equal(p1 == tiers.T3, p2 == tiers.T3) or np.array_equal(p1, p2):
+        bad.append("prop1_setup")
+    r1 = tiers.restricted_decode(q, K, V, tiers.kept_tokens(p1, s))
+    r2 = tiers.restricted_decode(q, K, V, tiers.kept_tokens(p2, s))
+    if not (np.array_equal(r1[0], r2[0]) and np.array_equal(r1[1], r2[1])):
+        bad.append("prop1")
+    return bad

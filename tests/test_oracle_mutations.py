@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import pins
-from oracle import attention, blocks, e4m3, footprint, paged, scores
+from oracle import attention, blocks, e4m3, footprint, paged, scores, tiers
 
 
 def _all_pins_pass() -> bool:
@@ -29,7 +29,8 @@ def _all_pins_pass() -> bool:
             and pins.score_failures() == []
             and pins.fp8_quant_failures() == []
             and pins.fp8_append_failures() == []
-            and pins.block_manager_failures() == [])
+            and pins.block_manager_failures() == []
+            and pins.tier_failures() == [])
 
 
 def _modulo_heads(h, n_q, n_kv):
@@ -181,6 +182,23 @@ def _release_ignoring_holders(self, b):
         self.free.append(b)
 
 
+def _plan_lowest_first(scores, protect_first, protect_last, t0_blocks, t1_blocks):
+    return _orig_plan(-np.asarray(scores), protect_first, protect_last, t0_blocks, t1_blocks)
+
+
+_orig_plan = tiers.plan_tiers
+
+
+def _restricted_ignores_mask(q, K, V, keep):
+    return attention.decode_sequence(q, np.asarray(K), np.asarray(V))
+
+
+def _block_scores_max(token_scores, s):
+    x = np.asarray(token_scores, dtype=np.float64)[:s]
+    nb = -(-s // 16)
+    return np.array([x[b * 16:min(s, (b + 1) * 16)].max() for b in range(nb)])
+
+
 MUTATIONS = [
     ("heads modulo instead of grouped", attention, "head_group", _modulo_heads),
     ("logit scale dropped", attention, "logits", _no_scale_logits),
@@ -202,6 +220,9 @@ MUTATIONS = [
     ("evicts the most recently released", blocks.BlockPool, "_take", _take_most_recent),
     ("finished blocks not kept for reuse", blocks.BlockPool, "_release", _release_to_free_list),
     ("release ignores other holders", blocks.BlockPool, "_release", _release_ignoring_holders),
+    ("tiers ranked lowest score first", tiers, "plan_tiers", _plan_lowest_first),
+    ("restricted decode ignores the kept set", tiers, "restricted_decode", _restricted_ignores_mask),
+    ("block score is the max, not the sum", tiers, "block_scores", _block_scores_max),
 ]
 
 

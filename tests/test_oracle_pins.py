@@ -121,6 +121,10 @@ def test_block_manager():
     assert pins.block_manager_failures() == []
 
 
+def test_tier_restricted_decode():
+    assert pins.tier_failures() == []
+
+
 @pytest.mark.parametrize("g", [1, 2, 4, 8])
 @pytest.mark.parametrize("d", [64, 128])
 def test_brute_force_grid(g, d):
