@@ -82,6 +82,10 @@ EXPORTS = {
     "kvd_bm_counts": (ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                       ctypes.POINTER(ctypes.c_int32)),
     "kvd_bm_refcount": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)),
+    "kvd_tier_block_scores": (ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p),
+    "kvd_tier_plan": (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                      ctypes.c_int32, ctypes.c_void_p),
+    "kvd_tier_restrict": (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p),
 }
 
 
@@ -452,3 +456,40 @@ class BlockManager:
         r = ctypes.c_int32()
         _check(lib.kvd_bm_refcount(self.handle, int(block), ctypes.byref(r)), "kvd_bm_refcount")
         return r.value
+
+
+# ---------------------------------------------------------------- tiers
+KVD_TIER_T0, KVD_TIER_T1, KVD_TIER_T3 = 0, 1, 3
+
+
+def tier_block_scores(token_scores):
+    """Per-block sums (float64 numpy) of one sequence's token scores (host fp32)."""
+    import numpy as np
+    ts = np.ascontiguousarray(np.asarray(token_scores, dtype=np.float32))
+    n = int(ts.shape[0])
+    out = np.zeros(max(-(-n // BLOCK_SIZE), 1), dtype=np.float64)
+    _check(lib.kvd_tier_block_scores(ts.ctypes.data, n, out.ctypes.data), "kvd_tier_block_scores")
+    return out[:-(-n // BLOCK_SIZE)]
+
+
+def tier_plan(block_scores, protect_first: int, protect_last: int, t0_blocks: int, t1_blocks: int):
+    """Tier (KVD_TIER_*) of every block, int8 numpy."""
+    import numpy as np
+    sc = np.ascontiguousarray(np.asarray(block_scores, dtype=np.float64))
+    nb = int(sc.shape[0])
+    out = np.zeros(max(nb, 1), dtype=np.int8)
+    _check(lib.kvd_tier_plan(sc.ctypes.data, nb, int(protect_first), int(protect_last), int(t0_blocks),
+                             int(t1_blocks), out.ctypes.data), "kvd_tier_plan")
+    return out[:nb]
+
+
+def tier_restrict(table_row, tiers):
+    """The block-table row of a decode over T0 and T1 (T3 entries become -1)."""
+    import numpy as np
+    row = np.ascontiguousarray(np.asarray(table_row, dtype=np.int32))
+    t = np.ascontiguousarray(np.asarray(tiers, dtype=np.int8))
+    _require(row.shape == t.shape, "table row and tiers differ in length")
+    out = np.zeros(max(row.shape[0], 1), dtype=np.int32)
+    _check(lib.kvd_tier_restrict(row.ctypes.data, t.ctypes.data, int(row.shape[0]), out.ctypes.data),
+           "kvd_tier_restrict")
+    return out[:row.shape[0]]

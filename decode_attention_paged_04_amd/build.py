@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvdecode.so")
-SOURCES = ["api.hip", "decode.hip", "merge.hip", "write.hip", "blocks.cpp"]
+SOURCES = ["api.hip", "decode.hip", "merge.hip", "write.hip", "blocks.cpp", "tiers.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -54,6 +54,7 @@ struct PairRegs {
   u32x4 v[FP8 ? 1 : NM];                       // bf16 V: 16 B per lane per channel tile
   u32x2 v8[FP8 ? NM : 1];                      // FP8 V: 8 B per lane per channel tile
   float sK, sV;                                // FP8 scales of this lane's block
+  uint32_t drop;                               // bit k: block k of the pair is not attended
 };
 
 // k index group G of MFMA step c covers these 8 channels of q and K.
@@ -63,7 +64,7 @@ __device__ inline int qk_channel0(int c, int G) {
 }
 
 template <int D, bool FP8, bool FINAL, bool SCORES>
-__global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeLaunch a) {
+__global__ __launch_bounds__(64 * kWaves, FP8 ? 3 : 2) void decode_kernel(DecodeLaunch a) {
   using R = PairRegs<D, FP8>;
   constexpr int E = R::E;
   constexpr int NM = R::NM;
@@ -126,6 +127,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeLaunch a) 
     const int nvalid = min(32, ntok - (p << 5));
     const int32_t pid0 = live ? load_invariant(bt + 2 * p) : -1;
     const int32_t pid1 = live && nvalid > kBlock ? load_invariant(bt + 2 * p + 1) : -1;
+    // A negative entry marks a block that is not attended (its loads read
+    // nothing, and consume masks its tokens).
+    f.drop = (pid0 < 0 ? 1u : 0u) | (pid1 < 0 ? 2u : 0u);
     const uint32_t t0 = tile_pair_offset(pid0, j, a.num_blocks, a.n_kv, TPB);
     const uint32_t t1 = tile_pair_offset(pid1, j, a.num_blocks, a.n_kv, TPB);
     // K: S-tile t, row r16 -> block r16/8, in-block row 8*((r16/4)&1) + 4t + r16%4,
@@ -198,6 +202,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeLaunch a) 
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (e >= my_valid) xs[e] = -INFINITY;
+    }
+    // This lane's tokens lie in block G/2 of the pair.
+    if (f.drop && ((f.drop >> (G >> 1)) & 1u)) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[e] = -INFINITY;
     }
 
     if constexpr (SCORES) {

@@ -121,6 +121,12 @@ __device__ inline int score_slot(int t) {
   return (t & ~31) + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
 }
 
+// alpha of one head and token from its log2-domain score and lse; a head that
+// attended nothing (lse2 = -inf, every block dropped) gives 0, not NaN.
+__device__ inline float weight_of(float x, float lse2) {
+  return lse2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x - lse2);
+}
+
 // score[i][t] += weight / n_q * sum_h exp2(x[i][h][t] - lse2[i][h]) for t < s_i,
 // x being the log2-domain scaled scores the decode kernel stored.  Each thread
 // owns one token; the heads' loads are issued eight at a time so that they are
@@ -146,9 +152,9 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ lo
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = x[(size_t)(h + u) * stride];
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc += __builtin_amdgcn_exp2f(v[u] - ls[h + u]);
+    for (int u = 0; u < U; ++u) acc += weight_of(v[u], ls[h + u]);
   }
-  for (; h < n_q; ++h) acc += __builtin_amdgcn_exp2f(x[(size_t)h * stride] - ls[h]);
+  for (; h < n_q; ++h) acc += weight_of(x[(size_t)h * stride], ls[h]);
   score[(size_t)i * score_stride + t] += w_over_nq * acc;
 }
 

@@ -94,6 +94,38 @@ kvd_status kvd_bm_counts(const kvd_block_manager* bm, int32_t* free_blocks, int3
 /* Number of sequences whose tables hold a block. */
 kvd_status kvd_bm_refcount(const kvd_block_manager* bm, int32_t block, int32_t* refcount);
 
+/* ---- tiers of a tier-restricted decode ---------------------------------
+ * gist.science summary of "Not all thinking needs HBM", methodology 1-4:
+ * tokens are sorted by cumulative attention score (the score output of
+ * kvd_decode_attn) into T0 (kept in HBM, with the protected prompt, sinks
+ * and recent window), T1 (host memory at full precision, prefetched before
+ * every attention step) and the evicted tail T3, re-sorted every 64 decode
+ * steps; attention covers T0 and T1, so its result depends only on what was
+ * evicted (Proposition 1).  Here the unit is the 16-token block: a block's
+ * score is the sum of its tokens' scores (summed in double); the first
+ * protect_first and last protect_last blocks are T0; the others are ranked by
+ * score, highest first, equal scores by position, and the first t0_blocks go
+ * to T0, the next t1_blocks to T1, the rest to T3 (T2 is not used).  Moving
+ * T1 between host and device memory is the caller's business: a T1 block
+ * only has to be resident, anywhere in the pool, when the decode runs. */
+#define KVD_TIER_T0 0
+#define KVD_TIER_T1 1
+#define KVD_TIER_T3 3
+
+/* block_scores (host double [ceil(n_tokens / 16)]) from token_scores (host
+ * fp32 [n_tokens], e.g. one sequence's row of the cumulative score). */
+kvd_status kvd_tier_block_scores(const float* token_scores, int32_t n_tokens, double* block_scores);
+
+/* tiers (host int8 [n_blocks], KVD_TIER_*) of one sequence's blocks.  Scores
+ * must be finite. */
+kvd_status kvd_tier_plan(const double* block_scores, int32_t n_blocks, int32_t protect_first,
+                         int32_t protect_last, int32_t t0_blocks, int32_t t1_blocks, int8_t* tiers);
+
+/* out_row = table_row with every T3 entry replaced by -1: the block-table row
+ * of a decode over T0 and T1 (host int32 [n_blocks] both; in place allowed). */
+kvd_status kvd_tier_restrict(const int32_t* table_row, const int8_t* tiers, int32_t n_blocks,
+                             int32_t* out_row);
+
 #ifdef __cplusplus
 }
 #endif

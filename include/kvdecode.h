@@ -135,7 +135,14 @@ typedef struct {
   int32_t max_context_len;    /* host-known bound on every s_i (sizes the launch)     */
   const void* q;              /* device bf16 [b][n_q][head_dim], post-RoPE            */
   const int32_t* block_table; /* device int32 [b][max_blocks_per_seq]; entries at or  */
-                              /* past ceil(s_i / 16) are never read                   */
+                              /* past ceil(s_i / 16) are never read.  A negative     */
+                              /* entry marks a block that is not attended: its tokens */
+                              /* take no part and nothing of it is read (attention   */
+                              /* over a subset of blocks, e.g. the T0 and T1 tiers   */
+                              /* of "Not all thinking needs HBM", methodology 3);    */
+                              /* with every block dropped a head's output is 0 and   */
+                              /* its lse -inf.  Entries >= num_blocks read as zeros  */
+                              /* (the result is then undefined).                     */
   const int32_t* context_lens;/* device int32 [b]; s_i is clamped into               */
                               /* [0, min(max_context_len, 16 * max_blocks_per_seq)]  */
   void* out;                  /* device bf16 [b][n_q][head_dim]; s_i = 0 gives zeros  */
