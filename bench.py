@@ -213,6 +213,34 @@ class Workload:
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n / 1e3
 
+    def restrict(self, seed: int, t0_frac: float, t1_frac: float):
+        """Restrict every layer's decode to the T0 and T1 tiers of a plan made
+        from seeded block scores (first block and last two protected); the
+        algorithmic bytes become those of the kept blocks."""
+        kvd, torch, w = self.kvd, self.torch, self.w
+        rng = np.random.default_rng(seed)
+        table = self.table.copy()
+        kept_tokens = []
+        for i, s in enumerate(self.lens):
+            nb = -(-int(s) // 16)
+            plan = kvd.tier_plan(rng.random(nb), 1, 2, int(nb * t0_frac), int(nb * t1_frac))
+            table[i, :nb] = kvd.tier_restrict(self.table[i, :nb], plan)
+            kept = sum(min(16, int(s) - 16 * b) for b in range(nb) if plan[b] != kvd.KVD_TIER_T3)
+            kept_tokens.append(kept)
+        self.kept_fraction = sum(kept_tokens) / float(self.lens.sum())
+        self.table_t = torch.from_numpy(table).cuda()
+        per_tok = 2 * w.n_kv * w.head_dim * self.kv_bytes
+        ids = sum(-(-int(s) // 16) for s in self.lens)
+        self.launch_bytes = (per_tok * sum(kept_tokens) + w.b * 2 * w.n_q * w.head_dim * 2 + 4 * ids
+                             + (2 * w.n_kv * 4 * sum(-(-k // 16) for k in kept_tokens) if self.fp8 else 0))
+        self.step_bytes = w.layers * self.launch_bytes
+        self.args = [[kvd.make_args(self.q[l], self.table_t, self.lens_t, self.max_ctx, self.out[l],
+                                    chunk_tokens=self.chunk, workspace=self.ws, pool=self.pools[r])
+                      for l in range(w.layers)] for r in range(self.R)]
+        self.pargs = [[kvd.make_args(self.q[l], self.table_t, self.lens_t, self.max_ctx, None,
+                                     chunk_tokens=self.chunk, pool=self.pools[r], need_out=False)
+                       for l in range(w.layers)] for r in range(self.R)]
+
     def time_append(self, n: int) -> float:
         """Mean duration (s) of one kvd_write_kv call storing one token per
         sequence -- what a decode step writes per layer -- into each
@@ -349,6 +377,29 @@ def extra_entry(name: str, steps: int):
     return e
 
 
+def tiered_entry(name: str, layers: int, steps: int):
+    """The same batch decoded in full and restricted to T0 + T1 (about half the
+    blocks): the restricted step should cost about its kept bytes."""
+    out = {}
+    for label in ("full", "tiered"):
+        wl = Workload(name, 0, 1, layers=layers)
+        if label == "tiered":
+            wl.restrict(seed=11, t0_frac=0.25, t1_frac=0.25)
+        wl.capture()
+        secs = wl.time_steps(steps, 2)
+        launch_s = wl.time_launches(40)
+        out[label] = {"ms_per_step": round(secs / steps * 1e3, 4),
+                      "GBs": round(wl.step_bytes / (secs / steps) / 1e9, 1),
+                      "launch_us": round(launch_s * 1e6, 2),
+                      "launch_GBs": round(wl.launch_bytes / launch_s / 1e9, 1)}
+        if label == "tiered":
+            out[label]["kept_fraction"] = round(wl.kept_fraction, 4)
+        log(f"{name} {label}: {out[label]}")
+        wl.free()
+    out["workload"] = f"{name} ({layers} layers), full vs restricted to T0+T1"
+    return out
+
+
 def append_entry(name: str, calls: int):
     """Cost of the decode step's own write: one token per sequence per layer."""
     wl = Workload(name, 0, 1, layers=1)
@@ -375,6 +426,7 @@ def main():
     ap.add_argument("--extras", default="70b_shard,8b_prefix",
                     help="further workloads reported in the same line (comma list), or 'none'")
     ap.add_argument("--no-append", action="store_true", help="skip the append-cost entries")
+    ap.add_argument("--no-tiered", action="store_true", help="skip the tier-restricted entry")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -434,6 +486,9 @@ def main():
     if args.extras != "none":
         for name in args.extras.split(","):
             extras.append(extra_entry(name, 10))
+    tiered = None
+    if not args.no_tiered:
+        tiered = tiered_entry("8b_ragged", 8, 10)
     appends = []
     if not args.no_append:
         for name in ("8b_ragged", "8b_fp8_scores"):
@@ -463,6 +518,7 @@ def main():
         "cpu_baseline": cpu,
         "secondary": secondary,
         "extra": extras,
+        "tiered": tiered,
         "append": appends,
     }
     print(json.dumps(line), flush=True)
