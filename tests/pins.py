@@ -641,3 +641,65 @@ def tier_failures(seed=13) -> list:
     if not (np.array_equal(r1[0], r2[0]) and np.array_equal(r1[1], r2[1])):
         bad.append("prop1")
     return bad
+
+
+# ---------------------------------------------------------------- mixed precision
+def mixed_failures(seed=14) -> list:
+    """Mixed-precision rows: every pair one precision, every block once with its
+    precision bit, a pad only between an odd first run and a second run, the
+    context length; the step over a row's blocks equals the plain step over the
+    same tokens whatever their order, FP8 blocks entering as stored."""
+    from oracle import e4m3, mixed
+    rng = np.random.default_rng(seed)
+    bad = []
+    for _ in range(200):
+        n16, n8 = int(rng.integers(0, 7)), int(rng.integers(0, 7))
+        ids = rng.permutation(100)[:n16 + n8]
+        a, b = list(ids[:n16]), list(ids[n16:])
+        fp8_last = bool(rng.integers(2))
+        tail = int(rng.integers(1, 17))
+        row, s = mixed.arrange_row(a, b, fp8_last, tail)
+        if not mixed.pairs_homogeneous(row):
+            bad.append(("homogeneous", a, b, fp8_last))
+            break
+        real = [e for e in row if e >= 0]
+        if sorted(real) != sorted(a + [x | mixed.PRECISION_BIT for x in b]):
+            bad.append(("ids", a, b))
+            break
+        first = a if fp8_last else b
+        second = b if fp8_last else a
+        pads = row.count(-1)
+        if pads != (1 if second and len(first) % 2 else 0):
+            bad.append(("pad", a, b, fp8_last))
+            break
+        if row and (s != 16 * (len(row) - 1) + tail or row[-1] < 0):
+            bad.append(("length", a, b))
+            break
+    # a worked row: bf16 blocks 3, 8, 5 then FP8 blocks 2, 7 (the last holding 9 tokens)
+    row, s = mixed.arrange_row([3, 8, 5], [2, 7], True, 9)
+    if row != [3, 8, 5, -1, 2 | (1 << 30), 7 | (1 << 30)] or s != 16 * 5 + 9:
+        bad.append(("worked", row, s))
+    # the step over the blocks, in any order, equals the plain step
+    n_q, n_kv, d, s = 4, 2, 16, 16 * 5 + 7
+    q = rng.standard_normal((n_q, d))
+    K = rng.standard_normal((s, n_kv, d)).astype(np.float32)
+    V = rng.standard_normal((s, n_kv, d)).astype(np.float32)
+    stored_K, stored_V = K.astype(np.float64).copy(), V.astype(np.float64).copy()
+    blocks = []
+    for b in range(6):
+        lo, hi = 16 * b, min(s, 16 * b + 16)
+        if b % 2:                                      # odd blocks stored as FP8
+            ck, sk = e4m3.quantize_sequence(K[lo:hi])
+            cv, sv = e4m3.quantize_sequence(V[lo:hi])
+            stored_K[lo:hi] = e4m3.dequantize_sequence(ck, sk)
+            stored_V[lo:hi] = e4m3.dequantize_sequence(cv, sv)
+        blocks.append((stored_K[lo:hi], stored_V[lo:hi]))
+    o_ref, l_ref = attention.decode_sequence(q, stored_K, stored_V)
+    for perm in (list(range(6)), [5, 0, 3, 1, 4, 2], [1, 3, 5, 0, 2, 4]):
+        o, l = mixed.decode_mixed(q, [blocks[k] for k in perm])
+        if np.max(np.abs(o - o_ref)) > 1e-13 or np.max(np.abs(l - l_ref)) > 1e-13:
+            bad.append(("order", perm))
+    o0, l0 = mixed.decode_mixed(q, [])
+    if np.any(o0 != 0) or not np.all(np.isneginf(l0)):
+        bad.append("empty")
+    return bad

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import pins
-from oracle import attention, blocks, e4m3, footprint, paged, scores, tiers
+from oracle import attention, blocks, e4m3, footprint, mixed, paged, scores, tiers
 
 
 def _all_pins_pass() -> bool:
@@ -30,7 +30,8 @@ def _all_pins_pass() -> bool:
             and pins.fp8_quant_failures() == []
             and pins.fp8_append_failures() == []
             and pins.block_manager_failures() == []
-            and pins.tier_failures() == [])
+            and pins.tier_failures() == []
+            and pins.mixed_failures() == [])
 
 
 def _modulo_heads(h, n_q, n_kv):
@@ -199,6 +200,20 @@ def _block_scores_max(token_scores, s):
     return np.array([x[b * 16:min(s, (b + 1) * 16)].max() for b in range(nb)])
 
 
+def _arrange_without_pad(ids_bf16, ids_fp8, fp8_last, tail_tokens):
+    first, second = (list(ids_bf16), list(ids_fp8)) if fp8_last else (list(ids_fp8), list(ids_bf16))
+    tf, ts = (0, 1 << 30) if fp8_last else (1 << 30, 0)
+    row = [b | tf for b in first] + [b | ts for b in second]
+    return (row, 16 * (len(row) - 1) + tail_tokens) if row else ([], 0)
+
+
+def _decode_mixed_drops_last(q, blocks):
+    return _orig_decode_mixed(q, blocks[:-1])
+
+
+_orig_decode_mixed = mixed.decode_mixed
+
+
 MUTATIONS = [
     ("heads modulo instead of grouped", attention, "head_group", _modulo_heads),
     ("logit scale dropped", attention, "logits", _no_scale_logits),
@@ -223,6 +238,8 @@ MUTATIONS = [
     ("tiers ranked lowest score first", tiers, "plan_tiers", _plan_lowest_first),
     ("restricted decode ignores the kept set", tiers, "restricted_decode", _restricted_ignores_mask),
     ("block score is the max, not the sum", tiers, "block_scores", _block_scores_max),
+    ("mixed row without the pad", mixed, "arrange_row", _arrange_without_pad),
+    ("mixed step drops a block", mixed, "decode_mixed", _decode_mixed_drops_last),
 ]
 
 

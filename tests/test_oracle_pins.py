@@ -125,6 +125,10 @@ def test_tier_restricted_decode():
     assert pins.tier_failures() == []
 
 
+def test_mixed_precision_rows():
+    assert pins.mixed_failures() == []
+
+
 @pytest.mark.parametrize("g", [1, 2, 4, 8])
 @pytest.mark.parametrize("d", [64, 128])
 def test_brute_force_grid(g, d):
