@@ -57,11 +57,9 @@ struct PairRegs {
   uint32_t drop;                               // bit k: block k of the pair is not attended
 };
 
-// k index group G of MFMA step c covers these 8 channels of q and K.
-template <int D, bool FP8>
-__device__ inline int qk_channel0(int c, int G) {
-  return FP8 ? (64 * (c >> 1) + 16 * G + 8 * (c & 1)) : (32 * c + 8 * G);
-}
+// k index group G of MFMA step c covers channels 32c + 8G .. +7 of q and K
+// (for bf16 and FP8 tiles alike: the K layout puts them in that lane).
+__device__ inline int qk_channel0(int c, int G) { return 32 * c + 8 * G; }
 
 template <int D, bool FP8, bool FINAL, bool SCORES>
 __global__ __launch_bounds__(64 * kWaves, FP8 ? 3 : 2) void decode_kernel(DecodeLaunch a) {
@@ -101,7 +99,7 @@ __global__ __launch_bounds__(64 * kWaves, FP8 ? 3 : 2) void decode_kernel(Decode
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (head_ok) raw = *reinterpret_cast<const u32x4*>(qrow + qk_channel0<D, FP8>(cc, G));
+      if (head_ok) raw = *reinterpret_cast<const u32x4*>(qrow + qk_channel0(cc, G));
       qf[cc] = __builtin_bit_cast(bf16x8, raw);
     }
   }

@@ -59,16 +59,23 @@ __host__ __device__ inline uint32_t tile_pair_offset(int32_t p, int32_t j, int32
 
 // Element offsets inside a tile pair (w = elem_bytes, n = 16 / w elements per
 // 16 bytes, P = head_dim / n pieces per row).  The K tile is stored as 16-byte
-// pieces in the operand order of the decode kernels' q.K^T MFMA: piece
-// (s * P + q) * 8 + r holds channels q n .. q n + n - 1 of in-block row
-// 8 (r / 4) + 4 s + r % 4, so the 32 lanes that read one block in one load
-// instruction read 512 contiguous bytes.  The V tile is channel-major: 16
-// consecutive rows of each channel.
+// pieces in the operand order of the decode kernels' q.K^T MFMA.  Channel c
+// belongs to MFMA step c / 32 and lane group (c / 8) % 4; a piece holds the
+// 8-channel slices of one lane group for n / 8 consecutive steps (one for
+// bf16, two for FP8): piece 4 (step / (n/8)) + group of the row, position
+// 8 (step % (n/8)) + c % 8.  Row t's piece q is piece (s * P + q) * 8 + r of
+// the tile, s = (t / 4) % 2, r = 4 (t / 8) + t % 4, so the 32 lanes that read
+// one block in one load instruction read 512 contiguous bytes, and bf16 and
+// FP8 tiles put the same channels in the same lanes.  The V tile is
+// channel-major: 16 consecutive rows of each channel.
 __host__ __device__ inline uint32_t k_elem(int row, int ch, int head_dim, int elem_bytes) {
   const int n = 16 / elem_bytes;
+  const int per = n / 8;
   const int s = (row >> 2) & 1;
   const int r = ((row >> 3) << 2) | (row & 3);
-  return (uint32_t)(((s * (head_dim / n) + ch / n) * 8 + r) * n + ch % n);
+  const int step = ch >> 5, group = (ch >> 3) & 3;
+  const int q = 4 * (step / per) + group;
+  return (uint32_t)(((s * (head_dim / n) + q) * 8 + r) * n + 8 * (step % per) + (ch & 7));
 }
 __host__ __device__ inline uint32_t v_elem(int row, int ch, int head_dim) {
   return (uint32_t)(16 * head_dim + ch * 16 + row);

@@ -73,8 +73,11 @@ typedef struct {
  *   tile pair of (layer l, physical block p, KV head j) starts at element
  *       T = ((l * num_blocks + p) * n_kv + j) * (2 * 16 * head_dim)
  *   K of in-block row t (0..15), channel c, with n = 16 / w elements per 16
- *   bytes, P = head_dim / n, s = (t / 4) % 2, r = 4 (t / 8) + t % 4:
- *       T + ((s * P + c / n) * 8 + r) * n + c % n
+ *   bytes, P = head_dim / n, s = (t / 4) % 2, r = 4 (t / 8) + t % 4,
+ *   k = n / 8 (MFMA steps per piece), step = c / 32, grp = (c / 8) % 4,
+ *   q = 4 (step / k) + grp:
+ *       T + ((s * P + q) * 8 + r) * n + 8 (step % k) + c % 8
+ *   (for bf16, k = 1 and q = c / 8: piece q holds channels 8q .. 8q + 7)
  *   V of in-block row t,         channel c:  T + 16 * head_dim + c * 16 + t
  *
  * so one (block, head) is one contiguous 2*16*head_dim*w-byte region: the K

@@ -14,11 +14,13 @@ of the library's code:
 
 * element offset of the tile pair of (layer l, physical block p, KV head j):
   ``((l * num_blocks + p) * n_kv + j) * 2 * 16 * head_dim``
-* K is kept as 16-byte pieces of n = 16 / w channels (w the element size,
-  P = head_dim / n pieces per row); row t's channel c lies in piece q = c // n
-  of the row, and with s = (t // 4) % 2 and r = 4 (t // 8) + t % 4 that
-  piece is piece number (s P + q) 8 + r of the tile, channel c sitting at
-  position c % n inside it;
+* K is kept as 16-byte pieces of n = 16 / w elements (w the element size,
+  P = head_dim / n pieces per row).  Channel c has step c // 32 and group
+  (c // 8) % 4; a piece holds n / 8 consecutive steps' 8-channel slices of
+  one group, so c lies in piece q = 4 (step // (n / 8)) + group of its row,
+  at position 8 (step % (n / 8)) + c % 8; with s = (t // 4) % 2 and
+  r = 4 (t // 8) + t % 4, piece q of row t is piece number (s P + q) 8 + r
+  of the tile (for bf16 a piece is simply channels 8q .. 8q + 7);
 * V of in-block row t, channel c: ``+ 16 * head_dim + c * 16 + t`` (channel-major)
 * FP8 pools use the same rules with w = 1 (offsets in bytes); the fp32 scale
   of (l, p, j) is at index ``((l * num_blocks + p) * n_kv + j) * 2`` (+0 for
@@ -62,11 +64,14 @@ class PoolLayout:
     def k_in_tile(self, row, ch):
         """Element offset of K[row][ch] from the start of its tile (works on arrays)."""
         n = 16 // self.elem_bytes
+        steps_per_piece = n // 8
         pieces_per_row = self.head_dim // n
         s = (row // 4) % 2
         r = 4 * (row // 8) + row % 4
-        piece = (s * pieces_per_row + ch // n) * 8 + r
-        return piece * n + ch % n
+        step, group = ch // 32, (ch // 8) % 4
+        q = 4 * (step // steps_per_piece) + group
+        piece = (s * pieces_per_row + q) * 8 + r
+        return piece * n + 8 * (step % steps_per_piece) + ch % 8
 
     @property
     def tile_pair_elems(self) -> int:
