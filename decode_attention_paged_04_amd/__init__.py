@@ -56,6 +56,8 @@ EXPORTS = {
     "kvd_decode_workspace_bytes": (ctypes.c_void_p, ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)),
     "kvd_decode_attn": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs), ctypes.c_void_p),
     "kvd_decode_attn_fp8": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs), ctypes.c_void_p),
+    "kvd_decode_attn_mixed": (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs),
+                              ctypes.c_void_p),
     "kvd_decode_partials": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs), ctypes.c_void_p,
                             ctypes.c_void_p, ctypes.c_void_p),
     "kvd_merge_partials": (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -86,6 +88,9 @@ EXPORTS = {
     "kvd_tier_plan": (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                       ctypes.c_int32, ctypes.c_void_p),
     "kvd_tier_restrict": (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p),
+    "kvd_mixed_row": (ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                      ctypes.POINTER(ctypes.c_int32)),
 }
 
 
@@ -291,6 +296,29 @@ def kvd_decode_attn_fp8(pool: Pool, layer: int, args: DecodeArgs, stream=None):
            "kvd_decode_attn_fp8")
 
 
+def kvd_decode_attn_mixed(pool_bf16: Pool, pool_fp8: Pool, layer: int, args: DecodeArgs, stream=None):
+    """Decode over bf16 blocks of ``pool_bf16`` and FP8 blocks of ``pool_fp8``
+    (table entries of FP8 blocks carry bit 30; see kvd_mixed_row)."""
+    _require(pool_fp8.desc.n_kv == pool_bf16.desc.n_kv and pool_fp8.desc.head_dim == pool_bf16.desc.head_dim,
+             "the two pools differ in shape")
+    _check(lib.kvd_decode_attn_mixed(pool_bf16.handle, pool_fp8.handle, layer, ctypes.byref(args),
+                                     _stream(stream)), "kvd_decode_attn_mixed")
+
+
+def decode_mixed(pool_bf16: Pool, pool_fp8: Pool, layer: int, q, block_table, context_lens,
+                 max_context_len: int, out=None, lse_out=None, chunk_tokens: int = 0, workspace=None,
+                 stream=None):
+    """Convenience: allocate out/workspace as needed and run one mixed-precision decode."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    args = make_args(q, block_table, context_lens, max_context_len, out, lse_out, chunk_tokens,
+                     workspace, pool=pool_bf16)
+    ws = workspace if workspace is not None else allocate_workspace(pool_bf16, args, device=q.device)
+    kvd_decode_attn_mixed(pool_bf16, pool_fp8, layer, args, stream)
+    return out, ws
+
+
 def kvd_decode_partials(pool: Pool, layer: int, q, block_table, context_lens, max_context_len: int,
                         part_o=None, part_lse=None, chunk_tokens: int = 0, stream=None):
     """Per-chunk partials (fp32 o_c ``[b][n_q][n_chunks][d]``, lse_c ``[b][n_q][n_chunks]``).
@@ -493,3 +521,21 @@ def tier_restrict(table_row, tiers):
     _check(lib.kvd_tier_restrict(row.ctypes.data, t.ctypes.data, int(row.shape[0]), out.ctypes.data),
            "kvd_tier_restrict")
     return out[:row.shape[0]]
+
+
+# ---------------------------------------------------------------- mixed precision
+PRECISION_BIT = 1 << 30
+
+
+def mixed_row(ids_bf16, ids_fp8, fp8_last: bool, tail_tokens: int):
+    """(row int32 numpy, context length) of one sequence for kvd_decode_attn_mixed."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(ids_bf16, dtype=np.int32))
+    b = np.ascontiguousarray(np.asarray(ids_fp8, dtype=np.int32))
+    cap = int(a.shape[0] + b.shape[0] + 1)
+    row = np.zeros(cap, dtype=np.int32)
+    n, s = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.kvd_mixed_row(a.ctypes.data, int(a.shape[0]), b.ctypes.data, int(b.shape[0]), 1 if fp8_last else 0,
+                             int(tail_tokens), row.ctypes.data, cap, ctypes.byref(n), ctypes.byref(s)),
+           "kvd_mixed_row")
+    return row[:n.value], s.value

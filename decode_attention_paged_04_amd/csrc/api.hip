@@ -114,13 +114,22 @@ kvd_status plan_decode(const PoolView& p, const kvd_decode_args* a, DecodePlan* 
 
 // One decode call.  ext_part_o / ext_part_lse (both or neither): write the
 // per-chunk partials there and stop, instead of producing the merged output.
+// pool8 (mixed precision only): the FP8 pool beside the bf16 pool `pool`.
 kvd_status decode_common(const kvd_pool* pool, int32_t layer, const kvd_decode_args* a,
                          void* stream, bool any_dtype, kvd_dtype want, float* ext_part_o,
-                         float* ext_part_lse) {
+                         float* ext_part_lse, const kvd_pool* pool8 = nullptr) {
   if (!pool || !a) return KVD_ERR_INVALID_ARG;
   const PoolView& p = pool->v;
   if (!any_dtype && p.dtype != want) return KVD_ERR_DTYPE;
   if (layer < 0 || layer >= p.num_layers) return KVD_ERR_INVALID_ARG;
+  if (pool8) {
+    const PoolView& p8 = pool8->v;
+    if (p8.dtype != KVD_FP8_E4M3) return KVD_ERR_DTYPE;
+    if (p8.num_layers != p.num_layers || p8.n_kv != p.n_kv || p8.head_dim != p.head_dim)
+      return KVD_ERR_INVALID_ARG;
+    if (p.num_blocks >= kvd::kPrecisionBit || p8.num_blocks >= kvd::kPrecisionBit) return KVD_ERR_UNSUPPORTED;
+    if (a->score) return KVD_ERR_UNSUPPORTED;
+  }
   const bool external = ext_part_o != nullptr || ext_part_lse != nullptr;
   if (external && (a->score || !ext_part_o || !ext_part_lse)) return KVD_ERR_INVALID_ARG;
   DecodePlan pl;
@@ -168,7 +177,16 @@ kvd_status decode_common(const kvd_pool* pool, int32_t layer, const kvd_decode_a
   L.logit_stride = pl.logit_stride;
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_stale_error();
-  KVD_TRY_HIP(kvd::launch_decode(L, p.head_dim, p.dtype == KVD_FP8_E4M3, final_direct, scores, s));
+  int kind = p.dtype == KVD_FP8_E4M3 ? kvd::kFp8 : kvd::kBf16;
+  if (pool8) {
+    const PoolView& p8 = pool8->v;
+    kind = kvd::kMixed;
+    L.layer_base8 = p8.kv_base + (size_t)layer * (size_t)p8.layer_bytes;
+    L.layer_bytes8 = (uint32_t)p8.layer_bytes;
+    L.layer_scales8 = p8.scale_base + (size_t)layer * p8.num_blocks * p8.n_kv * 2;
+    L.num_blocks8 = p8.num_blocks;
+  }
+  KVD_TRY_HIP(kvd::launch_decode(L, p.head_dim, kind, final_direct, scores, s));
   if (external) return KVD_OK;
   if (!final_direct) {
     KVD_TRY_HIP(kvd::launch_merge(L.part_o, L.part_lse, a->context_lens, pl.ctx_bound, pl.chunk, a->b,
@@ -268,6 +286,12 @@ kvd_status kvd_decode_attn(const kvd_pool* pool, int32_t layer, const kvd_decode
 kvd_status kvd_decode_attn_fp8(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
                                void* hip_stream) {
   return decode_common(pool, layer, args, hip_stream, false, KVD_FP8_E4M3, nullptr, nullptr);
+}
+
+kvd_status kvd_decode_attn_mixed(const kvd_pool* pool_bf16, const kvd_pool* pool_fp8, int32_t layer,
+                                 const kvd_decode_args* args, void* hip_stream) {
+  if (!pool_fp8) return KVD_ERR_INVALID_ARG;
+  return decode_common(pool_bf16, layer, args, hip_stream, false, KVD_BF16, nullptr, nullptr, pool_fp8);
 }
 
 kvd_status kvd_decode_partials(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,

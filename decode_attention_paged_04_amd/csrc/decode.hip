@@ -37,6 +37,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace kvd {
 
 constexpr int kWaves = 4;
@@ -61,13 +63,18 @@ struct PairRegs {
 // (for bf16 and FP8 tiles alike: the K layout puts them in that lane).
 __device__ inline int qk_channel0(int c, int G) { return 32 * c + 8 * G; }
 
-template <int D, bool FP8, bool FINAL, bool SCORES>
-__global__ __launch_bounds__(64 * kWaves, FP8 ? 3 : 2) void decode_kernel(DecodeLaunch a) {
-  using R = PairRegs<D, FP8>;
-  constexpr int E = R::E;
-  constexpr int NM = R::NM;
+// KIND: kBf16 or kFp8 (one pool), or kMixed (a bf16 and an FP8 pool; each
+// table entry names its block's precision in kPrecisionBit -- the page header
+// -- and the two entries of a pair share it).  A mixed kernel runs its pairs
+// twice, a bf16 pass and an FP8 pass; in each pass a pair of the other
+// precision is skipped like a dropped block, so every pass keeps the
+// one-precision pipeline (fixed loads in flight, one register set) and the
+// softmax state carries from the first pass into the second.
+template <int D, int KIND, bool FINAL, bool SCORES>
+__global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kernel(DecodeLaunch a) {
+  constexpr bool MIX = KIND == kMixed;
+  constexpr int NM = D / 16;                   // 16-channel tiles of the output
   constexpr int NC = D / 32;                   // MFMA steps along the head dim
-  constexpr uint32_t TPB = 2u * kBlock * D * E;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -105,6 +112,7 @@ __global__ __launch_bounds__(64 * kWaves, FP8 ? 3 : 2) void decode_kernel(Decode
   }
 
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.layer_base, a.layer_bytes);
+  const __amdgpu_buffer_rsrc_t rs8 = make_rsrc(MIX ? a.layer_base8 : a.layer_base, MIX ? a.layer_bytes8 : 0u);
   const int32_t* bt = a.block_table + (size_t)i * a.max_blocks + lo / kBlock;
   const float qk_scale = kLog2e * (1.0f / sqrtf((float)D));
 
@@ -116,197 +124,223 @@ __global__ __launch_bounds__(64 * kWaves, FP8 ? 3 : 2) void decode_kernel(Decode
 
   const int npairs = (ntok + 31) >> 5;
 
-  // Issue every load of pair p into f.  A pair past the end (p >= npairs)
-  // issues the same loads at out-of-range offsets: they return zeros without
-  // touching memory, and the number of loads in flight stays the same on every
-  // path, so the waits before each use cover exactly the pair being used.
-  auto issue = [&](R& f, int p) {
-    const bool live = p < npairs;
-    const int nvalid = min(32, ntok - (p << 5));
-    const int32_t pid0 = live ? load_invariant(bt + 2 * p) : -1;
-    const int32_t pid1 = live && nvalid > kBlock ? load_invariant(bt + 2 * p + 1) : -1;
-    // A negative entry marks a block that is not attended (its loads read
-    // nothing, and consume masks its tokens).
-    f.drop = (pid0 < 0 ? 1u : 0u) | (pid1 < 0 ? 2u : 0u);
-    const uint32_t t0 = tile_pair_offset(pid0, j, a.num_blocks, a.n_kv, TPB);
-    const uint32_t t1 = tile_pair_offset(pid1, j, a.num_blocks, a.n_kv, TPB);
-    // K: S-tile t, row r16 -> block r16/8, in-block row 8*((r16/4)&1) + 4t + r16%4,
-    // whose 16-byte unit u for lane group G (piece 4u + G of the row) is K piece
-    // ((t*KU + u)*4 + G)*8 + r16%8 of the block: each load reads 512 contiguous
-    // bytes per block.
-    const uint32_t tk = r16 < 8 ? t0 : t1;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int u = 0; u < R::KU; ++u) {
-        const uint32_t off = tk + (uint32_t)((((t * R::KU + u) * 4 + G) * 8 + (r16 & 7)) * 16);
-        f.k[t][u] = load16(rs, tk == kOutOfRange ? kOutOfRange : off);
+  // One pass over this wave's pairs, all of precision F8.
+  auto run = [&](auto f8tag) {
+    constexpr bool F8 = decltype(f8tag)::value;
+    using R = PairRegs<D, F8>;
+    constexpr int EE = R::E;                           // bytes per element
+    constexpr uint32_t TPB = 2u * kBlock * D * EE;     // bytes per (block, head) tile pair
+    constexpr bool OTHER = MIX && F8;                  // the mixed kernel's FP8 pool
+    const __amdgpu_buffer_rsrc_t rx = OTHER ? rs8 : rs;
+
+    // Issue every load of pair p into f.  A pair past the end (p >= npairs)
+    // issues the same loads at out-of-range offsets: they return zeros without
+    // touching memory, and the number of loads in flight stays the same on every
+    // path, so the waits before each use cover exactly the pair being used.
+    auto issue = [&](R& f, int p) {
+      const bool live = p < npairs;
+      const int nvalid = min(32, ntok - (p << 5));
+      int32_t pid0 = live ? load_invariant(bt + 2 * p) : -1;
+      int32_t pid1 = live && nvalid > kBlock ? load_invariant(bt + 2 * p + 1) : -1;
+      if constexpr (MIX) {
+        // A block of the other precision waits for the other pass.
+        if (pid0 >= 0) pid0 = ((pid0 & kPrecisionBit) != 0) == F8 ? (pid0 & ~kPrecisionBit) : -1;
+        if (pid1 >= 0) pid1 = ((pid1 & kPrecisionBit) != 0) == F8 ? (pid1 & ~kPrecisionBit) : -1;
       }
-    }
-    // V (channel-major): channel tile mm, channel 16mm + r16, rows 8(G&1) .. +7
-    // of block G/2.
-    const uint32_t tv = G < 2 ? t0 : t1;
-#pragma unroll
-    for (int mm = 0; mm < NM; ++mm) {
-      const uint32_t off = tv + (uint32_t)((v_elem(8 * (G & 1), 16 * mm + r16, D)) * E);
-      const uint32_t o2 = tv == kOutOfRange ? kOutOfRange : off;
-      if constexpr (FP8) f.v8[mm] = load8(rs, o2);
-      else f.v[mm] = load16(rs, o2);
-    }
-    if constexpr (FP8) {
-      // fp32 scales of this lane's block (G/2) for K and V; zero for a bad id.
-      const float* sc = a.layer_scales;
-      const float sk0 = t0 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid0 * a.n_kv + j) * 2 + 0);
-      const float sv0 = t0 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid0 * a.n_kv + j) * 2 + 1);
-      const float sk1 = t1 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid1 * a.n_kv + j) * 2 + 0);
-      const float sv1 = t1 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid1 * a.n_kv + j) * 2 + 1);
-      f.sK = G < 2 ? sk0 : sk1;
-      f.sV = G < 2 ? sv0 : sv1;
-    }
-  };
+      // A negative entry marks a block that is not attended (its loads read
+      // nothing, and consume masks its tokens).
+      f.drop = (pid0 < 0 ? 1u : 0u) | (pid1 < 0 ? 2u : 0u);
+      const uint32_t t0 = tile_pair_offset(pid0, j, OTHER ? a.num_blocks8 : a.num_blocks, a.n_kv, TPB);
+      const uint32_t t1 = tile_pair_offset(pid1, j, OTHER ? a.num_blocks8 : a.num_blocks, a.n_kv, TPB);
+      // K: S-tile t, row r16 -> block r16/8, in-block row 8*((r16/4)&1) + 4t + r16%4,
+      // whose 16-byte unit u for lane group G (piece 4u + G of the row) is K piece
+      // ((t*KU + u)*4 + G)*8 + r16%8 of the block: each load reads 512 contiguous
+      // bytes per block.
+      const uint32_t tk = r16 < 8 ? t0 : t1;
+  #pragma unroll
+      for (int t = 0; t < 2; ++t) {
+  #pragma unroll
+        for (int u = 0; u < R::KU; ++u) {
+          const uint32_t off = tk + (uint32_t)((((t * R::KU + u) * 4 + G) * 8 + (r16 & 7)) * 16);
+          f.k[t][u] = load16(rx, tk == kOutOfRange ? kOutOfRange : off);
+        }
+      }
+      // V (channel-major): channel tile mm, channel 16mm + r16, rows 8(G&1) .. +7
+      // of block G/2.
+      const uint32_t tv = G < 2 ? t0 : t1;
+  #pragma unroll
+      for (int mm = 0; mm < NM; ++mm) {
+        const uint32_t off = tv + (uint32_t)((v_elem(8 * (G & 1), 16 * mm + r16, D)) * EE);
+        const uint32_t o2 = tv == kOutOfRange ? kOutOfRange : off;
+        if constexpr (F8) f.v8[mm] = load8(rx, o2);
+        else f.v[mm] = load16(rx, o2);
+      }
+      if constexpr (F8) {
+        // fp32 scales of this lane's block (G/2) for K and V; zero for a bad id.
+        const float* sc = OTHER ? a.layer_scales8 : a.layer_scales;
+        const float sk0 = t0 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid0 * a.n_kv + j) * 2 + 0);
+        const float sv0 = t0 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid0 * a.n_kv + j) * 2 + 1);
+        const float sk1 = t1 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid1 * a.n_kv + j) * 2 + 0);
+        const float sv1 = t1 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid1 * a.n_kv + j) * 2 + 1);
+        f.sK = G < 2 ? sk0 : sk1;
+        f.sV = G < 2 ? sv0 : sv1;
+      }
+    };
 
-  // Fold pair p (held in f) into the running state.
-  auto consume = [&](R& f, int p) {
-    const int tok0 = p << 5;
-    const int nvalid = min(32, ntok - tok0);
+    // Fold pair p (held in f) into the running state.
+    auto consume = [&](R& f, int p) {
+      const int tok0 = p << 5;
+      const int nvalid = min(32, ntok - tok0);
+      // A pair with both blocks dropped adds nothing (its scores, when stored,
+      // are still written as -inf below).
+      if constexpr (!SCORES) {
+        if (f.drop == 3u) return;
+      }
 
-    f32x4 sacc[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        bf16x8 kf;
-        if constexpr (FP8) {
-          const u32x4 w = f.k[t][cc >> 1];
-          kf = (cc & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
+      f32x4 sacc[2];
+  #pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+          bf16x8 kf;
+          if constexpr (F8) {
+            const u32x4 w = f.k[t][cc >> 1];
+            kf = (cc & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
+          } else {
+            kf = __builtin_bit_cast(bf16x8, f.k[t][cc]);
+          }
+          sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[cc], sacc[t], 0, 0, 0);
+        }
+      }
+
+      // Scaled scores; lane element e = 4t + q is pair token 8G + e.
+      float xs[8];
+      const float sc_all = F8 ? qk_scale * f.sK : qk_scale;
+  #pragma unroll
+      for (int t = 0; t < 2; ++t)
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) xs[4 * t + q] = sacc[t][q] * sc_all;
+
+      const int my_valid = min(8, max(0, nvalid - 8 * G));   // valid tokens among my 8
+      if (nvalid < 32) {
+  #pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= my_valid) xs[e] = -INFINITY;
+      }
+      // This lane's tokens lie in block G/2 of the pair.
+      if (f.drop && ((f.drop >> (G >> 1)) & 1u)) {
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) xs[e] = -INFINITY;
+      }
+
+      if constexpr (SCORES) {
+        // Scaled scores of this head and pair, stored pair-permuted (see
+        // score_slot): the lanes' first halves form one contiguous 64-byte run,
+        // their second halves the next, so each store instruction writes whole
+        // runs.
+        if (head_ok) {
+          float* dst = a.logits + ih * a.logit_stride + lo + tok0 + 4 * G;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{xs[0], xs[1], xs[2], xs[3]};
+          *reinterpret_cast<f32x4*>(dst + 16) = f32x4{xs[4], xs[5], xs[6], xs[7]};
+        }
+      }
+
+      float mx = xs[0];
+  #pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, xs[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float corr = __builtin_amdgcn_exp2f(m - m_use);
+      m = m_new;
+
+      float pv[8];
+      float psum = 0.f;
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(xs[e] - m_use);
+        psum += pv[e];
+      }
+      l = l * corr + psum;
+  #pragma unroll
+      for (int mm = 0; mm < NM; ++mm) o[mm] *= corr;
+
+      bf16x8 phi, plo;
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = F8 ? pv[e] * f.sV : pv[e];
+        const __bf16 h = (__bf16)pe;
+        phi[e] = h;
+        plo[e] = (__bf16)(pe - (float)h);
+      }
+
+      // Zero V of tokens past the end so that stale (even NaN) rows contribute 0.
+      if (nvalid < 32) {
+        if constexpr (F8) {
+          uint32_t keep[2];
+  #pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            uint32_t mk = 0;
+  #pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+              if (4 * w + bb < my_valid) mk |= 0xFFu << (8 * bb);
+            keep[w] = mk;
+          }
+  #pragma unroll
+          for (int mm = 0; mm < NM; ++mm) {
+            f.v8[mm][0] &= keep[0];
+            f.v8[mm][1] &= keep[1];
+          }
         } else {
-          kf = __builtin_bit_cast(bf16x8, f.k[t][cc]);
+          uint32_t keep[4];
+  #pragma unroll
+          for (int w = 0; w < 4; ++w)
+            keep[w] = (2 * w < my_valid ? 0x0000FFFFu : 0u) | (2 * w + 1 < my_valid ? 0xFFFF0000u : 0u);
+  #pragma unroll
+          for (int mm = 0; mm < NM; ++mm)
+  #pragma unroll
+            for (int w = 0; w < 4; ++w) f.v[mm][w] &= keep[w];
         }
-        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[cc], sacc[t], 0, 0, 0);
       }
-    }
 
-    // Scaled scores; lane element e = 4t + q is pair token 8G + e.
-    float xs[8];
-    const float sc_all = FP8 ? qk_scale * f.sK : qk_scale;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) xs[4 * t + q] = sacc[t][q] * sc_all;
-
-    const int my_valid = min(8, max(0, nvalid - 8 * G));   // valid tokens among my 8
-    if (nvalid < 32) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e >= my_valid) xs[e] = -INFINITY;
-    }
-    // This lane's tokens lie in block G/2 of the pair.
-    if (f.drop && ((f.drop >> (G >> 1)) & 1u)) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xs[e] = -INFINITY;
-    }
-
-    if constexpr (SCORES) {
-      // Scaled scores of this head and pair, stored pair-permuted (see
-      // score_slot): the lanes' first halves form one contiguous 64-byte run,
-      // their second halves the next, so each store instruction writes whole
-      // runs.
-      if (head_ok) {
-        float* dst = a.logits + ih * a.logit_stride + lo + tok0 + 4 * G;
-        *reinterpret_cast<f32x4*>(dst) = f32x4{xs[0], xs[1], xs[2], xs[3]};
-        *reinterpret_cast<f32x4*>(dst + 16) = f32x4{xs[4], xs[5], xs[6], xs[7]};
+      // O^T[channel][head] += V^T P^T, rows = channels 16mm + 4G + q, cols = heads.
+  #pragma unroll
+      for (int mm = 0; mm < NM; ++mm) {
+        bf16x8 vf;
+        if constexpr (F8) vf = e4m3x8_to_bf16x8(f.v8[mm][0], f.v8[mm][1]);
+        else vf = __builtin_bit_cast(bf16x8, f.v[mm]);
+        o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi, o[mm], 0, 0, 0);
+        o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo, o[mm], 0, 0, 0);
       }
-    }
+    };
 
-    float mx = xs[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, xs[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float corr = __builtin_amdgcn_exp2f(m - m_use);
-    m = m_new;
-
-    float pv[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pv[e] = __builtin_amdgcn_exp2f(xs[e] - m_use);
-      psum += pv[e];
-    }
-    l = l * corr + psum;
-#pragma unroll
-    for (int mm = 0; mm < NM; ++mm) o[mm] *= corr;
-
-    bf16x8 phi, plo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = FP8 ? pv[e] * f.sV : pv[e];
-      const __bf16 h = (__bf16)pe;
-      phi[e] = h;
-      plo[e] = (__bf16)(pe - (float)h);
-    }
-
-    // Zero V of tokens past the end so that stale (even NaN) rows contribute 0.
-    if (nvalid < 32) {
-      if constexpr (FP8) {
-        uint32_t keep[2];
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          uint32_t mk = 0;
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb)
-            if (4 * w + bb < my_valid) mk |= 0xFFu << (8 * bb);
-          keep[w] = mk;
-        }
-#pragma unroll
-        for (int mm = 0; mm < NM; ++mm) {
-          f.v8[mm][0] &= keep[0];
-          f.v8[mm][1] &= keep[1];
-        }
-      } else {
-        uint32_t keep[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          keep[w] = (2 * w < my_valid ? 0x0000FFFFu : 0u) | (2 * w + 1 < my_valid ? 0xFFFF0000u : 0u);
-#pragma unroll
-        for (int mm = 0; mm < NM; ++mm)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) f.v[mm][w] &= keep[w];
+    // Two register sets: the next pair's loads are in flight while the current
+    // pair is consumed.  This wave owns pairs wave, wave + kWaves, ...; they are
+    // taken two at a time so that every pass through the loop has the same
+    // loads outstanding (a load past the end is an out-of-range no-op).
+    const int nmine = npairs > wave ? (npairs - wave + kWaves - 1) / kWaves : 0;
+    if (nmine > 0) {
+      R fa, fb;
+      int p = wave;
+      issue(fa, p);
+      int k = 0;
+      for (; k + 1 < nmine; k += 2) {
+        issue(fb, p + kWaves);
+        consume(fa, p);
+        issue(fa, p + 2 * kWaves);
+        consume(fb, p + kWaves);
+        p += 2 * kWaves;
       }
-    }
-
-    // O^T[channel][head] += V^T P^T, rows = channels 16mm + 4G + q, cols = heads.
-#pragma unroll
-    for (int mm = 0; mm < NM; ++mm) {
-      bf16x8 vf;
-      if constexpr (FP8) vf = e4m3x8_to_bf16x8(f.v8[mm][0], f.v8[mm][1]);
-      else vf = __builtin_bit_cast(bf16x8, f.v[mm]);
-      o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi, o[mm], 0, 0, 0);
-      o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo, o[mm], 0, 0, 0);
+      if (k < nmine) consume(fa, p);
     }
   };
-
-  // Two register sets: the next pair's loads are in flight while the current
-  // pair is consumed.  This wave owns pairs wave, wave + kWaves, ...; they are
-  // taken two at a time so that every pass through the loop has the same
-  // loads outstanding (a load past the end is an out-of-range no-op).
-  const int nmine = npairs > wave ? (npairs - wave + kWaves - 1) / kWaves : 0;
-  if (nmine > 0) {
-    R fa, fb;
-    int p = wave;
-    issue(fa, p);
-    int k = 0;
-    for (; k + 1 < nmine; k += 2) {
-      issue(fb, p + kWaves);
-      consume(fa, p);
-      issue(fa, p + 2 * kWaves);
-      consume(fb, p + kWaves);
-      p += 2 * kWaves;
-    }
-    if (k < nmine) consume(fa, p);
+  if constexpr (MIX) {
+    run(std::false_type{});
+    run(std::true_type{});
+  } else {
+    run(std::integral_constant<bool, KIND == kFp8>{});
   }
 
   // Whole-head sum of this wave.
@@ -363,28 +397,37 @@ __global__ __launch_bounds__(64 * kWaves, FP8 ? 3 : 2) void decode_kernel(Decode
   }
 }
 
-template <int D, bool FP8>
+template <int D, int KIND>
 static hipError_t launch_d(const DecodeLaunch& a, bool final_direct, bool scores,
                            hipStream_t stream) {
   const dim3 grid((unsigned)((size_t)a.n_chunks * a.b * a.n_kv));
   const dim3 block(64 * kWaves);
-  if (final_direct) {
-    if (scores) hipLaunchKernelGGL((decode_kernel<D, FP8, true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_kernel<D, FP8, true, false>), grid, block, 0, stream, a);
+  if constexpr (KIND == kMixed) {
+    // no fused score in a mixed-precision decode (rejected on the host)
+    if (final_direct) hipLaunchKernelGGL((decode_kernel<D, KIND, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_kernel<D, KIND, false, false>), grid, block, 0, stream, a);
+  } else if (final_direct) {
+    if (scores) hipLaunchKernelGGL((decode_kernel<D, KIND, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_kernel<D, KIND, true, false>), grid, block, 0, stream, a);
   } else {
-    if (scores) hipLaunchKernelGGL((decode_kernel<D, FP8, false, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_kernel<D, FP8, false, false>), grid, block, 0, stream, a);
+    if (scores) hipLaunchKernelGGL((decode_kernel<D, KIND, false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_kernel<D, KIND, false, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeLaunch& a, int head_dim, bool fp8, bool final_direct,
+template <int D>
+static hipError_t launch_kind(const DecodeLaunch& a, int kind, bool final_direct, bool scores,
+                              hipStream_t stream) {
+  if (kind == kMixed) return launch_d<D, kMixed>(a, final_direct, scores, stream);
+  if (kind == kFp8) return launch_d<D, kFp8>(a, final_direct, scores, stream);
+  return launch_d<D, kBf16>(a, final_direct, scores, stream);
+}
+
+hipError_t launch_decode(const DecodeLaunch& a, int head_dim, int kind, bool final_direct,
                          bool scores, hipStream_t stream) {
-  if (head_dim == 128)
-    return fp8 ? launch_d<128, true>(a, final_direct, scores, stream)
-               : launch_d<128, false>(a, final_direct, scores, stream);
-  return fp8 ? launch_d<64, true>(a, final_direct, scores, stream)
-             : launch_d<64, false>(a, final_direct, scores, stream);
+  return head_dim == 128 ? launch_kind<128>(a, kind, final_direct, scores, stream)
+                         : launch_kind<64>(a, kind, final_direct, scores, stream);
 }
 
 }  // namespace kvd

@@ -33,6 +33,11 @@ struct DecodePlan {
 };
 
 // Arguments handed to the decode kernel.
+// Pool kinds of a decode launch, and the table-entry bit that marks an FP8
+// block in a mixed-precision decode.
+constexpr int kBf16 = 0, kFp8 = 1, kMixed = 2;
+constexpr int32_t kPrecisionBit = 1 << 30;
+
 struct DecodeLaunch {
   const char* layer_base;   // start of this layer's tile pairs
   uint32_t layer_bytes;     // bytes addressable from layer_base
@@ -49,9 +54,14 @@ struct DecodeLaunch {
   float* logits;            // scores: log2-domain scaled logits [b][n_q][logit_stride]
   float* lse2;              // scores: log2-domain lse [b][n_q]
   int32_t logit_stride;
+  // mixed precision: the FP8 pool's layer, its scales and block count
+  const char* layer_base8;
+  uint32_t layer_bytes8;
+  const float* layer_scales8;
+  int32_t num_blocks8;
 };
 
-hipError_t launch_decode(const DecodeLaunch& a, int head_dim, bool fp8, bool final_direct,
+hipError_t launch_decode(const DecodeLaunch& a, int head_dim, int kind, bool final_direct,
                          bool scores, hipStream_t stream);
 
 hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_t* context_lens,

@@ -69,3 +69,37 @@ kvd_status kvd_tier_restrict(const int32_t* table_row, const int8_t* tiers, int3
 }
 
 }  // extern "C"
+
+// Mixed-precision rows (kvd_decode_attn_mixed): tier-homogeneous pages of two
+// entries, the precision bit on FP8 entries.
+extern "C" kvd_status kvd_mixed_row(const int32_t* ids_bf16, int32_t n_bf16, const int32_t* ids_fp8,
+                                    int32_t n_fp8, int32_t fp8_last, int32_t tail_tokens, int32_t* row,
+                                    int32_t capacity, int32_t* n_entries, int32_t* context_len) {
+  constexpr int32_t kBit = 1 << 30;
+  if (n_bf16 < 0 || n_fp8 < 0 || capacity < 0 || !n_entries || !context_len) return KVD_ERR_INVALID_ARG;
+  if ((n_bf16 > 0 && !ids_bf16) || (n_fp8 > 0 && !ids_fp8)) return KVD_ERR_INVALID_ARG;
+  if (fp8_last != 0 && fp8_last != 1) return KVD_ERR_INVALID_ARG;
+  const int32_t* first = fp8_last ? ids_bf16 : ids_fp8;
+  const int32_t* second = fp8_last ? ids_fp8 : ids_bf16;
+  const int32_t nf = fp8_last ? n_bf16 : n_fp8, ns = fp8_last ? n_fp8 : n_bf16;
+  const int32_t tf = fp8_last ? 0 : kBit, ts = fp8_last ? kBit : 0;
+  const int32_t pad = (ns > 0 && nf % 2) ? 1 : 0;
+  const int64_t n = (int64_t)nf + pad + ns;
+  *n_entries = (int32_t)n;
+  *context_len = 0;
+  if (n == 0) return KVD_OK;
+  if (tail_tokens < 1 || tail_tokens > 16) return KVD_ERR_INVALID_ARG;
+  if (n > capacity || !row) return KVD_ERR_INVALID_ARG;
+  int32_t k = 0;
+  for (int32_t i = 0; i < nf; ++i) {
+    if (first[i] < 0 || first[i] >= kBit) return KVD_ERR_INVALID_ARG;
+    row[k++] = first[i] | tf;
+  }
+  if (pad) row[k++] = -1;
+  for (int32_t i = 0; i < ns; ++i) {
+    if (second[i] < 0 || second[i] >= kBit) return KVD_ERR_INVALID_ARG;
+    row[k++] = second[i] | ts;
+  }
+  *context_len = 16 * (k - 1) + tail_tokens;
+  return KVD_OK;
+}

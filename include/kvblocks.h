@@ -126,6 +126,18 @@ kvd_status kvd_tier_plan(const double* block_scores, int32_t n_blocks, int32_t p
 kvd_status kvd_tier_restrict(const int32_t* table_row, const int8_t* tiers, int32_t n_blocks,
                              int32_t* out_row);
 
+/* One sequence's block-table row for kvd_decode_attn_mixed (tier-homogeneous
+ * pages): the first run's blocks (bf16 if fp8_last, else FP8), a -1 if that
+ * run has an odd length and a second run follows, then the second run's
+ * blocks; FP8 entries carry bit 30.  The row's last block holds tail_tokens
+ * (1..16) tokens, every other block 16, so *context_len = 16 * (entries - 1)
+ * + tail_tokens.  ids: host int32 block ids in [0, 2^30); row: host int32
+ * [capacity]; *n_entries is set even when capacity is too small
+ * (KVD_ERR_INVALID_ARG). */
+kvd_status kvd_mixed_row(const int32_t* ids_bf16, int32_t n_bf16, const int32_t* ids_fp8, int32_t n_fp8,
+                         int32_t fp8_last, int32_t tail_tokens, int32_t* row, int32_t capacity,
+                         int32_t* n_entries, int32_t* context_len);
+
 #ifdef __cplusplus
 }
 #endif

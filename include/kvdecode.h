@@ -198,6 +198,26 @@ kvd_status kvd_decode_attn(const kvd_pool* pool, int32_t layer, const kvd_decode
 kvd_status kvd_decode_attn_fp8(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
                                void* hip_stream);
 
+/* Decode over a mixed-precision block set: bf16 blocks in pool_bf16 and FP8
+ * E4M3 blocks in pool_fp8 (both with the same num_layers, n_kv, head_dim;
+ * fewer than 2^30 blocks each), following "The KV Cache Is the New Memory
+ * Wall" review §5.5 (one paged layout with a precision per block and a keep
+ * mask) and the gist.science summary of "Spherical KV" §2.2 (tier-homogeneous
+ * pages read in one header-guided pass).  Each block_table entry names its
+ * block's pool in bit 30 (set: pool_fp8, block = entry & ~(1 << 30)) -- the
+ * page header; a negative entry is a block that is not attended.  Entries
+ * 2k and 2k+1 of a row form a page that must hold one precision (pad with -1:
+ * a row lists one precision's blocks, a -1 if that run is odd, then the
+ * other's); a page mixing the two reads garbage (never out of bounds).  Only
+ * the final entry of a row may be partly filled.  The softmax covers the row's
+ * blocks whatever their order, so the output is the step over those tokens.
+ * No fused score (KVD_ERR_UNSUPPORTED: the rearranged row has no logical
+ * token positions).  Workspace, chunking and outputs as kvd_decode_attn (use
+ * pool_bf16 for kvd_decode_workspace_bytes).  KVD_ERR_DTYPE if pool_bf16 is
+ * not bf16 or pool_fp8 not FP8. */
+kvd_status kvd_decode_attn_mixed(const kvd_pool* pool_bf16, const kvd_pool* pool_fp8, int32_t layer,
+                                 const kvd_decode_args* args, void* hip_stream);
+
 /* Per-chunk partial results of one decode step of one layer, for a caller
  * that merges them itself -- for example the partials of context shards held
  * by several GPUs, combined with kvd_merge_partials.  Works on bf16 and FP8

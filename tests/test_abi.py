@@ -225,3 +225,16 @@ def test_auto_plan_fills_the_chip(b, n_kv, n_q, s, chunk):
     assert c % 16 == 0 and n == -(-s // c)
     assert c == chunk                   # the split measured best for these shapes
     assert b * n_kv * n >= 256          # at least one workgroup per compute unit
+
+
+def test_mixed_decode_errors():
+    p16, p8 = _pool(), _pool(kvd.KVD_FP8_E4M3)
+    a = _args()
+    f = kvd.lib.kvd_decode_attn_mixed
+    assert f(p16.handle, p8.handle, 0, ctypes.byref(_args(score=FAKE, score_stride=100)), None) == 2   # no score
+    assert f(p8.handle, p8.handle, 0, ctypes.byref(a), None) == 3          # first pool must be bf16
+    assert f(p16.handle, p16.handle, 0, ctypes.byref(a), None) == 3        # second pool must be FP8
+    assert f(p16.handle, _pool(kvd.KVD_FP8_E4M3, head_dim=64).handle, 0, ctypes.byref(a), None) == 1
+    assert f(p16.handle, _pool(kvd.KVD_FP8_E4M3, n_kv=4).handle, 0, ctypes.byref(a), None) == 1
+    assert f(p16.handle, None, 0, ctypes.byref(a), None) == 1
+    assert f(p16.handle, p8.handle, 5, ctypes.byref(a), None) == 1         # layer out of range

@@ -42,3 +42,20 @@ def test_errors():
         kvd.tier_plan(np.array([1.0]), -1, 0, 1, 1)
     with pytest.raises(kvd.KvdError):
         kvd.tier_restrict(np.array([1, 2], np.int32), np.array([0, 2], np.int8))
+
+
+def test_mixed_row_matches_oracle():
+    from oracle import mixed
+    rng = np.random.default_rng(9)
+    for _ in range(500):
+        n16, n8 = int(rng.integers(0, 9)), int(rng.integers(0, 9))
+        ids = rng.permutation(1000)[:n16 + n8]
+        fp8_last = bool(rng.integers(2))
+        tail = int(rng.integers(1, 17))
+        row, s = kvd.mixed_row(ids[:n16], ids[n16:], fp8_last, tail)
+        want_row, want_s = mixed.arrange_row(list(ids[:n16]), list(ids[n16:]), fp8_last, tail)
+        assert row.tolist() == want_row and s == want_s
+    with pytest.raises(kvd.KvdError):
+        kvd.mixed_row([1], [2], True, 0)                 # tail outside 1..16
+    with pytest.raises(kvd.KvdError):
+        kvd.mixed_row([1 << 30], [], True, 3)            # id does not fit below the bit
