@@ -400,6 +400,95 @@ def tiered_entry(name: str, layers: int, steps: int):
     return out
 
 
+def mixed_entry(name: str, layers: int, steps: int, fp8_share: float = 0.5):
+    """The batch with a seeded share of its blocks stored as FP8 (kvd_decode_attn_mixed):
+    rate over the bytes the two pools actually hold for it."""
+    import torch
+    import decode_attention_paged_04_amd as kvd
+    import workloads as W
+    w = W.WORKLOADS[name].with_(layers=layers)
+    lens = W.context_lengths(w)
+    rng = np.random.default_rng(w.seed + 77)
+    prec = [rng.random(-(-int(s) // 16)) < fp8_share for s in lens]
+    n8 = int(sum(p.sum() for p in prec))
+    n16 = int(sum(len(p) for p in prec)) - n8
+    pools = {False: kvd.allocate_pool(layers, max(n16, 1), w.n_kv, w.head_dim, kvd.KVD_BF16),
+             True: kvd.allocate_pool(layers, max(n8, 1), w.n_kv, w.head_dim, kvd.KVD_FP8_E4M3)}
+    phys = {False: rng.permutation(max(n16, 1)), True: rng.permutation(max(n8, 1))}
+    nxt = {False: 0, True: 0}
+    ids = []                                    # per sequence: physical id of each logical block
+    for p in prec:
+        row = []
+        for f8 in p:
+            row.append(int(phys[bool(f8)][nxt[bool(f8)]]))
+            nxt[bool(f8)] += 1
+        ids.append(row)
+    offs = W.offsets(lens)
+    n_tok = int(lens.sum())
+    slot = {False: np.full(n_tok, -1, np.int32), True: np.full(n_tok, -1, np.int32)}
+    for i, s in enumerate(lens):
+        for t in range(int(s)):
+            f8 = bool(prec[i][t // 16])
+            slot[f8][int(offs[i]) + t] = ids[i][t // 16] * 16 + t % 16
+    slot_t = {k: torch.from_numpy(v).cuda() for k, v in slot.items()}
+    qs = []
+    for layer in range(layers):
+        K, V = W.keys_values(w, layer, n_tok, "cuda")
+        for f8 in (False, True):
+            kvd.kvd_write_kv(pools[f8], layer, K, V, slot_t[f8])
+        qs.append(W.query(w, layer, "cuda"))
+        del K, V
+    rows, ctx = [], []
+    for i, s in enumerate(lens):
+        nb = len(prec[i])
+        r, c = kvd.mixed_row([ids[i][b] for b in range(nb) if not prec[i][b]],
+                             [ids[i][b] for b in range(nb) if prec[i][b]],
+                             bool(prec[i][nb - 1]), int(s) - 16 * (nb - 1))
+        rows.append(r)
+        ctx.append(c)
+    mb = max(len(r) for r in rows)
+    table = np.full((w.b, mb), -1, np.int32)
+    for i, r in enumerate(rows):
+        table[i, :len(r)] = r
+    table_t = torch.from_numpy(table).cuda()
+    ctx_t = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    outs = [torch.empty_like(q) for q in qs]
+    probe = kvd.make_args(qs[0], table_t, ctx_t, max(ctx), outs[0], pool=pools[False])
+    ws = kvd.allocate_workspace(pools[False], probe)
+    args = [kvd.make_args(qs[l], table_t, ctx_t, max(ctx), outs[l], workspace=ws, pool=pools[False])
+            for l in range(layers)]
+    def step():
+        h = int(torch.cuda.current_stream().cuda_stream)     # the capture stream inside a graph
+        for l in range(layers):
+            kvd.kvd_decode_attn_mixed(pools[False], pools[True], l, args[l], h)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    secs = (time.perf_counter() - t0) / steps
+    tok8 = sum(min(16, int(s) - 16 * b) for i, s in enumerate(lens) for b in range(len(prec[i])) if prec[i][b])
+    tok16 = n_tok - tok8
+    per_layer = (tok16 * 2 * w.n_kv * w.head_dim * 2 + tok8 * 2 * w.n_kv * w.head_dim
+                 + 2 * w.n_kv * 4 * n8 + 4 * (n16 + n8) + w.b * 2 * w.n_q * w.head_dim * 2)
+    res = {"workload": f"{w.name} ({layers} layers), {tok8 / n_tok:.1%} of tokens in FP8 blocks",
+           "ms_per_step": round(secs * 1e3, 4), "GBs": round(layers * per_layer / secs / 1e9, 1),
+           "bytes_per_step": layers * per_layer}
+    log(f"mixed: {res}")
+    del graph, pools, args, ws, outs, qs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def append_entry(name: str, calls: int):
     """Cost of the decode step's own write: one token per sequence per layer."""
     wl = Workload(name, 0, 1, layers=1)
@@ -427,6 +516,7 @@ def main():
                     help="further workloads reported in the same line (comma list), or 'none'")
     ap.add_argument("--no-append", action="store_true", help="skip the append-cost entries")
     ap.add_argument("--no-tiered", action="store_true", help="skip the tier-restricted entry")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-precision entry")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -489,6 +579,9 @@ def main():
     tiered = None
     if not args.no_tiered:
         tiered = tiered_entry("8b_ragged", 8, 10)
+    mixed = None
+    if not args.no_mixed:
+        mixed = mixed_entry("8b_ragged", 8, 10)
     appends = []
     if not args.no_append:
         for name in ("8b_ragged", "8b_fp8_scores"):
@@ -519,6 +612,7 @@ def main():
         "secondary": secondary,
         "extra": extras,
         "tiered": tiered,
+        "mixed": mixed,
         "append": appends,
     }
     print(json.dumps(line), flush=True)
