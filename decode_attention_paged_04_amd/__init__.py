@@ -4,7 +4,7 @@ Argument marshalling only: every step of the decode path runs in the HIP
 kernels of ``libkvdecode.so``.  PyTorch supplies device memory and streams.
 The functions keep the C names; see ``include/kvdecode.h`` for the layout,
 ownership and error rules.  Importing this package fails if the library has
-not been built (``python -m decode_attention_paged_04_amd.build``).
+not been built (``python decode_attention_paged_04_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -103,7 +103,7 @@ def _load():
     # fail with hipErrorNoDevice.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m decode_attention_paged_04_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python decode_attention_paged_04_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     for name, argtypes in EXPORTS.items():
         fn = getattr(lib, name)
