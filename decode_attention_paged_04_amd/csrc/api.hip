@@ -189,8 +189,8 @@ kvd_status decode_common(const kvd_pool* pool, int32_t layer, const kvd_decode_a
   KVD_TRY_HIP(kvd::launch_decode(L, p.head_dim, kind, final_direct, scores, s));
   if (external) return KVD_OK;
   if (!final_direct) {
-    KVD_TRY_HIP(kvd::launch_merge(L.part_o, L.part_lse, a->context_lens, pl.ctx_bound, pl.chunk, a->b,
-                          a->n_q, pl.n_chunks, p.head_dim, L.out, a->lse_out, L.lse2, s));
+    KVD_TRY_HIP(kvd::launch_merge(L.part_o, L.part_lse, a->b, a->n_q, pl.n_chunks, p.head_dim, L.out,
+                                  a->lse_out, L.lse2, s));
   }
   if (scores) {
     KVD_TRY_HIP(kvd::launch_score(L.logits, L.lse2, a->context_lens, pl.ctx_bound, a->b, a->n_q,
@@ -309,9 +309,8 @@ kvd_status kvd_merge_partials(const float* part_o, const float* part_lse, int32_
   if (!part_o || !part_lse || !out_bf16) return KVD_ERR_INVALID_ARG;
   if ((int64_t)b * n_q >= ((int64_t)1 << 31)) return KVD_ERR_UNSUPPORTED;
   clear_stale_error();
-  KVD_TRY_HIP(kvd::launch_merge(part_o, part_lse, nullptr, 0, 1, b, n_q, n_chunks, d_h,
-                        static_cast<uint16_t*>(out_bf16), lse_out, nullptr,
-                        static_cast<hipStream_t>(hip_stream)));
+  KVD_TRY_HIP(kvd::launch_merge(part_o, part_lse, b, n_q, n_chunks, d_h, static_cast<uint16_t*>(out_bf16),
+                                lse_out, nullptr, static_cast<hipStream_t>(hip_stream)));
   return KVD_OK;
 }
 

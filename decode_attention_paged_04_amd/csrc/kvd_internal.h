@@ -64,8 +64,7 @@ struct DecodeLaunch {
 hipError_t launch_decode(const DecodeLaunch& a, int head_dim, int kind, bool final_direct,
                          bool scores, hipStream_t stream);
 
-hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_t* context_lens,
-                        int32_t ctx_bound, int32_t chunk, int32_t b, int32_t n_q,
+hipError_t launch_merge(const float* part_o, const float* part_lse, int32_t b, int32_t n_q,
                         int32_t n_chunks, int32_t head_dim, uint16_t* out, float* lse_out,
                         float* lse2, hipStream_t stream);
 

@@ -24,10 +24,10 @@ __device__ inline float wave_sum(float v) {
 
 // One workgroup of four waves per (sequence, query head); wave w owns the
 // channels [w*D/4, (w+1)*D/4).  lse = M + ln(sum_c exp(lse_c - M)) with M =
-// max_c lse_c over the first nc chunks; out = sum_c exp(lse_c - lse) * o_c,
-// rounded to bf16.  A chunk whose weight is 0 (lse_c = -inf) is never read, so
-// its o_c may hold anything.  No chunk, or only empty ones: out = 0, lse =
-// -inf.
+// max_c lse_c over all n_chunks chunks; out = sum_c exp(lse_c - lse) * o_c,
+// rounded to bf16.  The o_c of a chunk whose weight is 0 (lse_c = -inf) is
+// loaded but never used, so it may hold anything, NaN included.  No chunk, or
+// only empty ones: out = 0, lse = -inf.
 // Every wave computes M and the sum itself with shuffles (no LDS, no
 // barrier), and all loads of a batch of up to kBatch chunks per lane are
 // issued before any is used, so a merge of a few dozen chunks costs about one
@@ -36,20 +36,15 @@ __device__ inline float wave_sum(float v) {
 // added with shuffles in a fixed order.
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ context_lens, int32_t ctx_bound, int32_t chunk, int32_t n_q,
-    int32_t n_chunks, uint16_t* __restrict__ out, float* __restrict__ lse_out,
-    float* __restrict__ lse2) {
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, int32_t n_chunks,
+    uint16_t* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ lse2) {
   constexpr int CH = D / 4;                      // channels per wave
   constexpr int NG = 64 / CH;                    // chunk groups per channel
   constexpr int kBatch = 16;                     // chunks per lane loaded at once
   const size_t ih = blockIdx.x;
-  int nc = n_chunks;
-  if (context_lens) {
-    int s = context_lens[ih / n_q];
-    s = s < 0 ? 0 : (s > ctx_bound ? ctx_bound : s);
-    nc = min(n_chunks, (s + chunk - 1) / chunk);
-  }
+  // Chunks past a sequence's end, or with nothing attended, carry lse -inf:
+  // they weigh 0, so no context length has to be read before the loads go out.
+  const int nc = n_chunks;
   const float* pl = part_lse + ih * n_chunks;
   const float* po = part_o + ih * n_chunks * D;
   const int lane = threadIdx.x & 63;
@@ -158,17 +153,16 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ lo
   score[(size_t)i * score_stride + t] += w_over_nq * acc;
 }
 
-hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_t* context_lens,
-                        int32_t ctx_bound, int32_t chunk, int32_t b, int32_t n_q,
+hipError_t launch_merge(const float* part_o, const float* part_lse, int32_t b, int32_t n_q,
                         int32_t n_chunks, int32_t head_dim, uint16_t* out, float* lse_out,
                         float* lse2, hipStream_t stream) {
   const dim3 grid((unsigned)((size_t)b * n_q));
   if (head_dim == 128)
     hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, part_o, part_lse,
-                       context_lens, ctx_bound, chunk, n_q, n_chunks, out, lse_out, lse2);
+                       n_chunks, out, lse_out, lse2);
   else
     hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, stream, part_o, part_lse,
-                       context_lens, ctx_bound, chunk, n_q, n_chunks, out, lse_out, lse2);
+                       n_chunks, out, lse_out, lse2);
   return hipGetLastError();
 }
 
