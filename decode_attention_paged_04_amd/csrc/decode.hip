@@ -63,6 +63,60 @@ struct PairRegs {
 // (for bf16 and FP8 tiles alike: the K layout puts them in that lane).
 __device__ inline int qk_channel0(int c, int G) { return 32 * c + 8 * G; }
 
+// Launch order of the (sequence, chunk) units.  Per KV head the grid holds
+// b * n_chunks units, n_chunks covering the longest allowed context, but a
+// sequence of s tokens fills only ceil(s / chunk) of its chunks.  Workgroup x
+// takes KV head x % n_kv and unit k = x / n_kv of this order: first every
+// chunk that holds tokens, sequence by sequence, then every empty chunk,
+// sequence by sequence.  An empty chunk only marks itself empty for the merge
+// (or writes a zero output); placed at the end of the grid, such workgroups no
+// longer hold compute units while chunks with tokens wait to be dispatched.
+// Each wave finds its unit itself: lane l reads the length of sequence
+// g0 + l, and a prefix sum over the lanes locates k.
+struct Unit {
+  int i, c, s;                                  // sequence, chunk, clamped context length
+};
+
+__device__ inline int wave_inclusive_sum(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+__device__ inline Unit locate_unit(const DecodeLaunch& a, int k) {
+  const int lane = threadIdx.x & 63;
+  auto length = [&](int q) {
+    int s = q < a.b ? a.context_lens[q] : 0;
+    return s < 0 ? 0 : (s > a.ctx_bound ? a.ctx_bound : s);
+  };
+  const int s0 = length(lane);                  // sequences 0..63, kept for the common case
+  int live_total = 0;
+  for (int g0 = 0; g0 < a.b; g0 += 64) {
+    const int sl = g0 == 0 ? s0 : length(g0 + lane);
+    live_total += __builtin_amdgcn_readfirstlane(__shfl(wave_inclusive_sum((sl + a.chunk - 1) / a.chunk), 63));
+  }
+  const bool live = k < live_total;
+  int kk = live ? k : k - live_total;
+  for (int g0 = 0; g0 < a.b; g0 += 64) {
+    const int sl = g0 == 0 ? s0 : length(g0 + lane);
+    const int nc = (sl + a.chunk - 1) / a.chunk;
+    const int cnt = g0 + lane < a.b ? (live ? nc : a.n_chunks - nc) : 0;
+    const int incl = wave_inclusive_sum(cnt);
+    const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));   // uniform: scalar branch
+    if (kk < total) {
+      const int li = __popcll(__ballot(incl <= kk));   // incl is non-decreasing over the lanes
+      const int excl = __shfl(incl - cnt, li);
+      return Unit{g0 + li, (live ? 0 : __shfl(nc, li)) + kk - excl, __shfl(sl, li)};
+    }
+    kk -= total;
+  }
+  return Unit{-1, 0, 0};
+}
+
 // KIND: kBf16 or kFp8 (one pool), or kMixed (a bf16 and an FP8 pool; each
 // table entry names its block's precision in kPrecisionBit -- the page header
 // -- and the two entries of a pair share it).  A mixed kernel runs its pairs
@@ -83,11 +137,12 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
 
   const int x = blockIdx.x;
   const int j = x % a.n_kv;
-  const int i = (x / a.n_kv) % a.b;
-  const int c = x / (a.n_kv * a.b);
-
-  int s = a.context_lens[i];
-  s = s < 0 ? 0 : (s > a.ctx_bound ? a.ctx_bound : s);
+  const Unit u = locate_unit(a, x / a.n_kv);
+  // the unit is the same for every lane: keep it in scalar registers
+  const int i = __builtin_amdgcn_readfirstlane(u.i);
+  const int c = __builtin_amdgcn_readfirstlane(u.c);
+  const int s = __builtin_amdgcn_readfirstlane(u.s);
+  if (i < 0) return;                            // outside the grid's units (not reached)
   const int lo = c * a.chunk;
   const int ntok = min(s, lo + a.chunk) - lo;
   const int g = a.g;

@@ -274,6 +274,47 @@ def test_decode_partials_match_oracle_chunks(env, fp8, chunk):
         H.assert_bf16_close(out, case.oracle(0)[0], what="merged single chunk")
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_large_batch_unit_order(env, fp8):
+    """150 sequences (more than one 64-lane group of lengths), a fifth of them
+    empty: the decode kernel places the chunks that hold tokens before the
+    empty ones, locating its unit with a prefix sum over every group.  Each
+    chunk's partial, the live/empty pattern, the merged output and the
+    single-chunk path must match the oracle."""
+    kvd, H, W, torch = env
+    from oracle import attention
+    rng = np.random.default_rng(41)
+    lens = rng.integers(1, 300, 150).astype(np.int32)
+    lens[rng.random(150) < 0.2] = 0
+    lens[[0, 63, 64, 127, 128, 149]] = [0, 299, 0, 1, 33, 0]     # group edges
+    w = W.DecodeWorkload("batch150", seed=42, b=150, layers=1, n_q=8, n_kv=2, head_dim=64,
+                         ctx=("fixed", 0), kv_dtype="fp8" if fp8 else "bf16")
+    case = _case(H, W, w, lens=lens)
+    qf = H.bf16_to_f64(case.q[0])
+    for chunk in (32, 96):
+        H.say(f"batch150 fp8={fp8} chunk={chunk}")
+        part_o, part_lse, C, nc = kvd.kvd_decode_partials(case.pool, 0, case.q[0], case.table_t, case.lens_t,
+                                                          case.max_ctx, chunk_tokens=chunk)
+        torch.cuda.synchronize()
+        po, pl = part_o.cpu().double().numpy(), part_lse.cpu().double().numpy()
+        for i, s in enumerate(lens):
+            K, V = case.logical(0, i)
+            oc, lc = attention.chunk_partials(qf[i], K, V, C, n_chunks=nc)
+            live = np.isfinite(lc)
+            assert np.array_equal(np.isneginf(pl[i]), ~live), (i, s)
+            if live.any():
+                err = np.abs(po[i][live] - oc[live]) / np.maximum(1.0, np.abs(oc[live]))
+                assert err.max() <= 1e-5, (i, s, err.max())
+    ref_o, ref_l = case.oracle(0)
+    for chunk in (0, 64, 512):                   # 512: one chunk, the direct path
+        out, lse = case.run(0, chunk=chunk)
+        torch.cuda.synchronize()
+        H.assert_bf16_close(out, ref_o, what=f"batch150 fp8={fp8} chunk={chunk}")
+        H.assert_lse_close(lse, ref_l)
+        empty = torch.from_numpy(lens == 0).cuda()
+        assert torch.all(out[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
+
+
 def test_bad_block_ids_read_as_zero(env):
     kvd, H, W, torch = env
     w = _workload(W, 4, 64, seed=500)
