@@ -66,13 +66,15 @@ __device__ inline int qk_channel0(int c, int G) { return 32 * c + 8 * G; }
 // Launch order of the (sequence, chunk) units.  Per KV head the grid holds
 // b * n_chunks units, n_chunks covering the longest allowed context, but a
 // sequence of s tokens fills only ceil(s / chunk) of its chunks.  Workgroup x
-// takes KV head x % n_kv and unit k = x / n_kv of this order: first every
-// chunk that holds tokens, sequence by sequence, then every empty chunk,
-// sequence by sequence.  An empty chunk only marks itself empty for the merge
-// (or writes a zero output); placed at the end of the grid, such workgroups no
-// longer hold compute units while chunks with tokens wait to be dispatched.
-// Each wave finds its unit itself: lane l reads the length of sequence
-// g0 + l, and a prefix sum over the lanes locates k.
+// takes KV head x % n_kv and unit k = x / n_kv of this order, in three runs,
+// each sequence by sequence: the full chunks, then the partly filled last
+// chunks, then the empty chunks.  The hardware hands out workgroups in grid
+// order, so the shorter units run last and the final workgroups drain sooner;
+// an empty chunk only marks itself empty for the merge (or writes a zero
+// output), and at the end of the grid such workgroups no longer hold compute
+// units while chunks with tokens wait.  Each wave finds its unit itself: lane
+// l reads the length of sequence g0 + l, and a prefix sum over the lanes
+// locates k within a run.
 struct Unit {
   int i, c, s;                                  // sequence, chunk, clamped context length
 };
@@ -94,23 +96,26 @@ __device__ inline Unit locate_unit(const DecodeLaunch& a, int k) {
     return s < 0 ? 0 : (s > a.ctx_bound ? a.ctx_bound : s);
   };
   const int s0 = length(lane);                  // sequences 0..63, kept for the common case
-  int live_total = 0;
+  int n_full = 0, n_part = 0;                   // units in the first two runs
   for (int g0 = 0; g0 < a.b; g0 += 64) {
     const int sl = g0 == 0 ? s0 : length(g0 + lane);
-    live_total += __builtin_amdgcn_readfirstlane(__shfl(wave_inclusive_sum((sl + a.chunk - 1) / a.chunk), 63));
+    n_full += __builtin_amdgcn_readfirstlane(__shfl(wave_inclusive_sum(sl / a.chunk), 63));
+    n_part += __builtin_amdgcn_readfirstlane(__shfl(wave_inclusive_sum(sl % a.chunk != 0 ? 1 : 0), 63));
   }
-  const bool live = k < live_total;
-  int kk = live ? k : k - live_total;
+  const int run = k < n_full ? 0 : (k < n_full + n_part ? 1 : 2);
+  int kk = run == 0 ? k : (run == 1 ? k - n_full : k - n_full - n_part);
   for (int g0 = 0; g0 < a.b; g0 += 64) {
     const int sl = g0 == 0 ? s0 : length(g0 + lane);
-    const int nc = (sl + a.chunk - 1) / a.chunk;
-    const int cnt = g0 + lane < a.b ? (live ? nc : a.n_chunks - nc) : 0;
+    const int full = sl / a.chunk;
+    const int part = sl % a.chunk != 0 ? 1 : 0;
+    const int first = run == 0 ? 0 : (run == 1 ? full : full + part);   // first chunk of the run
+    const int cnt = g0 + lane >= a.b ? 0 : (run == 0 ? full : (run == 1 ? part : a.n_chunks - full - part));
     const int incl = wave_inclusive_sum(cnt);
     const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));   // uniform: scalar branch
     if (kk < total) {
       const int li = __popcll(__ballot(incl <= kk));   // incl is non-decreasing over the lanes
       const int excl = __shfl(incl - cnt, li);
-      return Unit{g0 + li, (live ? 0 : __shfl(nc, li)) + kk - excl, __shfl(sl, li)};
+      return Unit{g0 + li, __shfl(first, li) + kk - excl, __shfl(sl, li)};
     }
     kk -= total;
   }
