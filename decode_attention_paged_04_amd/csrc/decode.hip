@@ -66,7 +66,7 @@ __device__ inline int qk_channel0(int c, int G) { return 32 * c + 8 * G; }
 // Launch order of the (sequence, chunk) units.  Per KV head the grid holds
 // b * n_chunks units, n_chunks covering the longest allowed context, but a
 // sequence of s tokens fills only ceil(s / chunk) of its chunks.  Workgroup x
-// takes one KV head and one unit k of this order (see the kernel), in three runs,
+// takes KV head x % n_kv and unit k = x / n_kv of this order, in three runs,
 // each sequence by sequence: the full chunks, then the partly filled last
 // chunks, then the empty chunks.  The hardware hands out workgroups in grid
 // order, so the shorter units run last and the final workgroups drain sooner;
@@ -140,20 +140,9 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
   const int G = lane >> 4;
   const int r16 = lane & 15;
 
-  // Workgroups reach the XCDs round-robin in grid order.  Consecutive groups
-  // of kXcds workgroups take kXcds consecutive units with one KV head, the
-  // next group the same units with the next head, and so on: all heads of a
-  // unit then run on one XCD, whose L2 serves the block-table lines and FP8
-  // scale lines (one line holds every head's scales of a block) once instead
-  // of once per head.  The last group holds the R < kXcds remaining units.
-  constexpr int kXcds = 8;
   const int x = blockIdx.x;
-  const int n_units = a.b * a.n_chunks;
-  const int grp = x / (kXcds * a.n_kv);
-  const int r_units = min(kXcds, n_units - grp * kXcds);
-  const int within = x - grp * kXcds * a.n_kv;
-  const int j = within / r_units;
-  const Unit u = locate_unit(a, grp * kXcds + within % r_units);
+  const int j = x % a.n_kv;
+  const Unit u = locate_unit(a, x / a.n_kv);
   // the unit is the same for every lane: keep it in scalar registers
   const int i = __builtin_amdgcn_readfirstlane(u.i);
   const int c = __builtin_amdgcn_readfirstlane(u.c);
