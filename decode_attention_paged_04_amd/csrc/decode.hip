@@ -237,11 +237,13 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
       }
       if constexpr (F8) {
         // fp32 scales of this lane's block (G/2) for K and V; zero for a bad id.
-        const float* sc = OTHER ? a.layer_scales8 : a.layer_scales;
-        const float sk0 = t0 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid0 * a.n_kv + j) * 2 + 0);
-        const float sv0 = t0 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid0 * a.n_kv + j) * 2 + 1);
-        const float sk1 = t1 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid1 * a.n_kv + j) * 2 + 0);
-        const float sv1 = t1 == kOutOfRange ? 0.f : load_invariant(sc + ((size_t)pid1 * a.n_kv + j) * 2 + 1);
+        // Head-major: this head's scales of all blocks are contiguous.
+        const float* sc = (OTHER ? a.layer_scales8 : a.layer_scales) +
+                          (size_t)j * (OTHER ? a.num_blocks8 : a.num_blocks) * 2;
+        const float sk0 = t0 == kOutOfRange ? 0.f : load_invariant(sc + (size_t)pid0 * 2 + 0);
+        const float sv0 = t0 == kOutOfRange ? 0.f : load_invariant(sc + (size_t)pid0 * 2 + 1);
+        const float sk1 = t1 == kOutOfRange ? 0.f : load_invariant(sc + (size_t)pid1 * 2 + 0);
+        const float sv1 = t1 == kOutOfRange ? 0.f : load_invariant(sc + (size_t)pid1 * 2 + 1);
         f.sK = G < 2 ? sk0 : sk1;
         f.sV = G < 2 ? sv0 : sv1;
       }

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64) void write_fp8_kernel(char* __restrict__ layer_
   const uint16_t* src = (which ? v : k) + ((size_t)t * n_kv + j) * D;
   const size_t row_stride = (size_t)n_kv * D;
   uint8_t* tile = reinterpret_cast<uint8_t*>(layer_base + ((size_t)p * n_kv + j) * (2 * kBlock * D));
-  float* scale_at = layer_scales + ((size_t)p * n_kv + j) * 2 + which;
+  float* scale_at = layer_scales + ((size_t)j * num_blocks + p) * 2 + which;   // head-major
   auto at = [&](int r, int ch) -> uint8_t& { return tile[which ? v_elem(r, ch, D) : k_elem(r, ch, D, 1)]; };
 
   const float s_old = r0 > 0 ? *scale_at : 0.f;

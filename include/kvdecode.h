@@ -85,8 +85,10 @@ typedef struct {
  * piece n channels of one row), then the V tile channel-major.  Logical token t of a
  * sequence lives in physical block table[t / 16] at in-block row t % 16.
  * FP8 pools add fp32 scales, one per (layer, block, KV head) for K and one
- * for V, at scale_base[((l * num_blocks + p) * n_kv + j) * 2 + {0: K, 1: V}];
- * a stored element decodes to code_value * scale.
+ * for V, head-major within a layer, at
+ * scale_base[((l * n_kv + j) * num_blocks + p) * 2 + {0: K, 1: V}], so that
+ * the scales one KV head reads are contiguous; a stored element decodes to
+ * code_value * scale.
  * Each layer of the pool must be smaller than 4 GiB. */
 typedef struct kvd_pool kvd_pool;
 

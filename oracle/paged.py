@@ -23,8 +23,8 @@ of the library's code:
   of the tile (for bf16 a piece is simply channels 8q .. 8q + 7);
 * V of in-block row t, channel c: ``+ 16 * head_dim + c * 16 + t`` (channel-major)
 * FP8 pools use the same rules with w = 1 (offsets in bytes); the fp32 scale
-  of (l, p, j) is at index ``((l * num_blocks + p) * n_kv + j) * 2`` (+0 for
-  K, +1 for V).
+  of (l, p, j) is at index ``((l * n_kv + j) * num_blocks + p) * 2`` (+0 for
+  K, +1 for V): head-major within a layer.
 """
 from __future__ import annotations
 
@@ -92,7 +92,7 @@ class PoolLayout:
                 + ch * BLOCK_SIZE + row)
 
     def scale_index(self, layer: int, block: int, head: int, which: int) -> int:
-        return ((layer * self.num_blocks + block) * self.n_kv + head) * 2 + which
+        return ((layer * self.n_kv + head) * self.num_blocks + block) * 2 + which
 
 
 def scatter(pool: np.ndarray, lay: PoolLayout, layer: int, table_row, K, V) -> None:

@@ -111,8 +111,9 @@ def test_t1_placement_does_not_change_the_result(env, fp8):
                 a, z = src * block_bytes, nxt * block_bytes
                 case.pool.kv[z:z + block_bytes] = case.pool.kv[a:a + block_bytes]
                 if fp8:
-                    case.pool.scales[nxt * lay.n_kv * 2:(nxt + 1) * lay.n_kv * 2] = \
-                        case.pool.scales[src * lay.n_kv * 2:(src + 1) * lay.n_kv * 2]
+                    for j in range(lay.n_kv):
+                        d0, s0 = lay.scale_index(0, nxt, j, 0), lay.scale_index(0, src, j, 0)
+                        case.pool.scales[d0:d0 + 2] = case.pool.scales[s0:s0 + 2]
                 moved[i, b] = nxt
                 nxt += 1
     assert nxt > case.num_blocks - spare                 # some T1 blocks were moved
