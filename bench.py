@@ -7,8 +7,8 @@ cached K/V once.  The headline workload is the Llama-3.1-8B-shaped single
 layer (b = 1, 32 query / 8 KV heads, head dim 128, s = 32,768); the
 Llama-3-70B-shaped long-context step (b = 4, 80 layers, s = 131,072, about
 172 GB of resident KV) is reported beside it, and the ragged 8B batch, the
-FP8 + fused-score batch, a context shard of the 70B step and a shared-prefix
-batch as further entries of the same line.
+FP8 + fused-score batch, a context shard of the 70B step, a shared-prefix
+batch and a 256-request serving batch as further entries of the same line.
 
 Reported:
 * value       -- algorithmic KV GB/s of the whole step (bytes the method must
@@ -514,7 +514,7 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="chunk_tokens (0 = the library's choice)")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas (0 = enough to exceed the cache)")
     ap.add_argument("--launches", type=int, default=200, help="event-timed launches for the roofline")
-    ap.add_argument("--extras", default="8b_ragged,8b_fp8_scores,70b_shard,8b_prefix",
+    ap.add_argument("--extras", default="8b_ragged,8b_fp8_scores,70b_shard,8b_prefix,8b_batch256",
                     help="further workloads reported in the same line (comma list), or 'none'")
     ap.add_argument("--no-append", action="store_true", help="skip the append-cost entries")
     ap.add_argument("--no-tiered", action="store_true", help="skip the tier-restricted entry")

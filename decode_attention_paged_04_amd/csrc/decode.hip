@@ -72,9 +72,12 @@ __device__ inline int qk_channel0(int c, int G) { return 32 * c + 8 * G; }
 // order, so the shorter units run last and the final workgroups drain sooner;
 // an empty chunk only marks itself empty for the merge (or writes a zero
 // output), and at the end of the grid such workgroups no longer hold compute
-// units while chunks with tokens wait.  Each wave finds its unit itself: lane
-// l reads the length of sequence g0 + l, and a prefix sum over the lanes
-// locates k within a run.
+// units while chunks with tokens wait.
+// Each wave finds its unit itself, in two rounds of loads whatever b is: lane
+// l owns sequences [l per, (l + 1) per), per = ceil(b / 64), and counts their
+// chunks of each kind (its loads are independent of one another); a prefix
+// sum over the lanes finds the lane that owns unit k, and a second prefix sum
+// over that lane's sequences finds the sequence and chunk.
 struct Unit {
   int i, c, s;                                  // sequence, chunk, clamped context length
 };
@@ -95,29 +98,47 @@ __device__ inline Unit locate_unit(const DecodeLaunch& a, int k) {
     int s = q < a.b ? a.context_lens[q] : 0;
     return s < 0 ? 0 : (s > a.ctx_bound ? a.ctx_bound : s);
   };
-  const int s0 = length(lane);                  // sequences 0..63, kept for the common case
-  int n_full = 0, n_part = 0;                   // units in the first two runs
-  for (int g0 = 0; g0 < a.b; g0 += 64) {
-    const int sl = g0 == 0 ? s0 : length(g0 + lane);
-    n_full += __builtin_amdgcn_readfirstlane(__shfl(wave_inclusive_sum(sl / a.chunk), 63));
-    n_part += __builtin_amdgcn_readfirstlane(__shfl(wave_inclusive_sum(sl % a.chunk != 0 ? 1 : 0), 63));
+  const int per = (a.b + 63) >> 6;              // sequences per lane
+  int nf = 0, np = 0, s1 = 0;                   // this lane's full and partly filled chunks
+#pragma unroll 8
+  for (int m = 0; m < per; ++m) {
+    const int sl = length(lane * per + m);
+    nf += sl / a.chunk;
+    np += sl % a.chunk != 0 ? 1 : 0;
+    s1 = sl;
   }
+  const int owned = max(0, min(a.b, (lane + 1) * per) - lane * per);
+  const int nd = owned * a.n_chunks - nf - np;  // its empty chunks
+  const int n_full = __builtin_amdgcn_readfirstlane(__shfl(wave_inclusive_sum(nf), 63));
+  const int n_part = __builtin_amdgcn_readfirstlane(__shfl(wave_inclusive_sum(np), 63));
   const int run = k < n_full ? 0 : (k < n_full + n_part ? 1 : 2);
-  int kk = run == 0 ? k : (run == 1 ? k - n_full : k - n_full - n_part);
-  for (int g0 = 0; g0 < a.b; g0 += 64) {
-    const int sl = g0 == 0 ? s0 : length(g0 + lane);
+  const int kk = run == 0 ? k : (run == 1 ? k - n_full : k - n_full - n_part);
+  const int cnt = run == 0 ? nf : (run == 1 ? np : nd);
+  const int incl = wave_inclusive_sum(cnt);
+  const int li = __popcll(__ballot(incl <= kk));       // incl is non-decreasing over the lanes
+  int kq = __builtin_amdgcn_readfirstlane(kk - __shfl(incl - cnt, li));   // index among lane li's units
+  auto first_of = [&](int sl) {                        // first chunk of the run in a sequence
+    const int full = sl / a.chunk;
+    return run == 0 ? 0 : (run == 1 ? full : full + (sl % a.chunk != 0 ? 1 : 0));
+  };
+  if (per == 1) {                                      // lane li owns just sequence li
+    const int sl = __shfl(s1, li);
+    return Unit{li, first_of(sl) + kq, sl};
+  }
+  for (int m0 = 0; m0 < per; m0 += 64) {
+    const int q = li * per + m0 + lane;
+    const bool in = m0 + lane < per && q < a.b;
+    const int sl = in ? length(q) : 0;
     const int full = sl / a.chunk;
     const int part = sl % a.chunk != 0 ? 1 : 0;
-    const int first = run == 0 ? 0 : (run == 1 ? full : full + part);   // first chunk of the run
-    const int cnt = g0 + lane >= a.b ? 0 : (run == 0 ? full : (run == 1 ? part : a.n_chunks - full - part));
-    const int incl = wave_inclusive_sum(cnt);
-    const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));   // uniform: scalar branch
-    if (kk < total) {
-      const int li = __popcll(__ballot(incl <= kk));   // incl is non-decreasing over the lanes
-      const int excl = __shfl(incl - cnt, li);
-      return Unit{g0 + li, __shfl(first, li) + kk - excl, __shfl(sl, li)};
+    const int c2 = !in ? 0 : (run == 0 ? full : (run == 1 ? part : a.n_chunks - full - part));
+    const int incl2 = wave_inclusive_sum(c2);
+    const int total = __builtin_amdgcn_readfirstlane(__shfl(incl2, 63));   // uniform: scalar branch
+    if (kq < total) {
+      const int mi = __popcll(__ballot(incl2 <= kq));
+      return Unit{li * per + m0 + mi, __shfl(first_of(sl), mi) + kq - __shfl(incl2 - c2, mi), __shfl(sl, mi)};
     }
-    kk -= total;
+    kq -= total;
   }
   return Unit{-1, 0, 0};
 }

@@ -74,6 +74,9 @@ WORKLOADS = {
     "8b_prefix": DecodeWorkload("llama3.1-8b-8layer-b32-shared16k+1k", seed=7, b=32, layers=8,
                                 n_q=32, n_kv=8, head_dim=128, ctx=("fixed", 17408),
                                 shared_prefix=16384),
+    # a large serving batch: 256 requests of 1k..4k tokens
+    "8b_batch256": DecodeWorkload("llama3.1-8b-32layer-b256-s1k..4k", seed=8, b=256, layers=32,
+                                  n_q=32, n_kv=8, head_dim=128, ctx=("uniform", 1024, 4096)),
     "8b_fp8_scores": DecodeWorkload("llama3.1-8b-fp8-scores-32layer-b32-s8k..32k", seed=5,
                                     b=32, layers=32, n_q=32, n_kv=8, head_dim=128,
                                     ctx=("uniform", 8192, 32768), kv_dtype="fp8",
