@@ -243,10 +243,11 @@ class Workload:
                                      chunk_tokens=self.chunk, pool=self.pools[r], need_out=False)
                        for l in range(w.layers)] for r in range(self.R)]
 
-    def time_append(self, n: int) -> float:
+    def time_append(self, n: int):
         """Mean duration (s) of one kvd_write_kv call storing one token per
         sequence -- what a decode step writes per layer -- into each
-        sequence's last block (a partly filled block re-quantises under FP8)."""
+        sequence's last block (a partly filled block re-quantises under FP8):
+        (eager calls from Python, calls replayed from a HIP graph)."""
         torch, kvd, w = self.torch, self.kvd, self.w
         last = torch.from_numpy(self.table[np.arange(w.b), (self.lens - 1) // 16] * 16 + (self.lens - 1) % 16)
         slots = last.to(torch.int32).cuda()
@@ -263,7 +264,27 @@ class Workload:
             kvd.kvd_write_kv(self.pools[0], k % w.layers, K, V, slots)
         b.record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / n / 1e3
+        eager = a.elapsed_time(b) / n / 1e3
+        per_graph = 16
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            kvd.kvd_write_kv(self.pools[0], 0, K, V, slots)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(per_graph):
+                kvd.kvd_write_kv(self.pools[0], k % w.layers, K, V, slots)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, n // per_graph)
+        a.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return eager, a.elapsed_time(b) / (reps * per_graph) / 1e3
 
     def config(self):
         w = self.w
@@ -494,10 +515,10 @@ def mixed_entry(name: str, layers: int, steps: int, fp8_share: float = 0.5):
 def append_entry(name: str, calls: int):
     """Cost of the decode step's own write: one token per sequence per layer."""
     wl = Workload(name, 0, 1, layers=1)
-    s = wl.time_append(calls)
+    eager, graphed = wl.time_append(calls)
     w = wl.w
     e = {"workload": f"{w.name} (1 layer)", "kv_dtype": w.kv_dtype, "tokens_per_call": w.b,
-         "us_per_call": round(s * 1e6, 2),
+         "us_per_call": round(graphed * 1e6, 2), "us_per_call_eager": round(eager * 1e6, 2),
          "stored_bytes_per_call": w.b * 2 * w.n_kv * w.head_dim * wl.kv_bytes}
     wl.free()
     return e

@@ -65,6 +65,9 @@ __device__ inline float e4m3_to_float(uint32_t code) {
 // scale, fp32) and the run's new rows.  Old codes are re-encoded from their
 // read-back values only if the scale changed; new rows are encoded under the
 // new scale.  A run starting at row 0 is the plain block quantisation.
+// Every load is issued before any is used (the slots around the entry, the old
+// scale, the old codes and the new rows), so a decode step's append costs about
+// two memory round trips: the loads, then the stores.
 template <int D>
 __global__ __launch_bounds__(64) void write_fp8_kernel(char* __restrict__ layer_base,
                                                        float* __restrict__ layer_scales,
@@ -73,19 +76,23 @@ __global__ __launch_bounds__(64) void write_fp8_kernel(char* __restrict__ layer_
                                                        const uint16_t* __restrict__ v,
                                                        const int32_t* __restrict__ slots,
                                                        int32_t n_tok) {
+  constexpr int CPL = D / 64;                       // channels per lane: lane, lane + 64
   const int t = blockIdx.x;
   const int j = blockIdx.y;
   const int which = blockIdx.z;                     // 0: K, 1: V
   const int lane = threadIdx.x;
   const int32_t slot = slots[t];
+  const int32_t prev = t > 0 ? slots[t - 1] : -2;
+  const int32_t next = lane < kBlock - 1 && t + 1 + lane < n_tok ? slots[t + 1 + lane] : -2;
   if (slot < 0) return;
   const int32_t p = slot / kBlock;
   if (p >= num_blocks) return;
   const int r0 = slot % kBlock;
-  // Only the first entry of a run does the work.
-  if (r0 != 0 && t > 0 && slots[t - 1] == slot - 1) return;
-  int n = 1;
-  while (r0 + n < kBlock && t + n < n_tok && slots[t + n] == slot + n) ++n;
+  // Only the first entry of a run does the work; the run goes on while the
+  // following entries take the next rows of the same block.
+  if (r0 != 0 && prev == slot - 1) return;
+  const uint64_t cont = __ballot(lane < kBlock - 1 - r0 && next == slot + 1 + lane);
+  const int n = 1 + __builtin_ctzll(~cont);
 
   const uint16_t* src = (which ? v : k) + ((size_t)t * n_kv + j) * D;
   const size_t row_stride = (size_t)n_kv * D;
@@ -94,27 +101,41 @@ __global__ __launch_bounds__(64) void write_fp8_kernel(char* __restrict__ layer_
   auto at = [&](int r, int ch) -> uint8_t& { return tile[which ? v_elem(r, ch, D) : k_elem(r, ch, D, 1)]; };
 
   const float s_old = r0 > 0 ? *scale_at : 0.f;
+  uint32_t old[kBlock][CPL];
+  float fresh[kBlock][CPL];
+#pragma unroll
+  for (int r = 0; r < kBlock; ++r) {
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      const int ch = lane + 64 * q;
+      old[r][q] = r < r0 ? (uint32_t)at(r, ch) : 0u;
+      fresh[r][q] = r < n ? bf16_bits_to_float(src[r * row_stride + ch]) : 0.f;
+    }
+  }
   float am = 0.f;
-  for (int r = 0; r < r0; ++r)
-    for (int ch = lane; ch < D; ch += 64) am = fmaxf(am, fabsf(e4m3_to_float(at(r, ch)) * s_old));
-  for (int r = 0; r < n; ++r)
-    for (int ch = lane; ch < D; ch += 64) am = fmaxf(am, fabsf(bf16_bits_to_float(src[r * row_stride + ch])));
+#pragma unroll
+  for (int r = 0; r < kBlock; ++r) {
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      if (r < r0) am = fmaxf(am, fabsf(e4m3_to_float(old[r][q]) * s_old));
+      if (r < n) am = fmaxf(am, fabsf(fresh[r][q]));
+    }
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
   const float scale = am / 448.0f;
 
-  if (r0 > 0 && scale != s_old) {
-    for (int r = 0; r < r0; ++r) {
-      for (int ch = lane; ch < D; ch += 64) {
-        const float x = e4m3_to_float(at(r, ch)) * s_old;
+  const bool reencode = r0 > 0 && scale != s_old;
+#pragma unroll
+  for (int r = 0; r < kBlock; ++r) {
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      const int ch = lane + 64 * q;
+      if (reencode && r < r0) {
+        const float x = e4m3_to_float(old[r][q]) * s_old;
         at(r, ch) = (uint8_t)(scale == 0.f ? 0u : e4m3_encode(x / scale));
       }
-    }
-  }
-  for (int r = 0; r < n; ++r) {
-    for (int ch = lane; ch < D; ch += 64) {
-      const float x = bf16_bits_to_float(src[r * row_stride + ch]);
-      at(r0 + r, ch) = (uint8_t)(scale == 0.f ? 0u : e4m3_encode(x / scale));
+      if (r < n) at(r0 + r, ch) = (uint8_t)(scale == 0.f ? 0u : e4m3_encode(fresh[r][q] / scale));
     }
   }
   if (lane == 0) *scale_at = scale;
