@@ -1,0 +1,77 @@
+"""Seeded random decode configurations on the GPU against the oracle.
+
+Each case draws a batch size, ragged context lengths (empty and one-token
+sequences included), a GQA shape (group sizes 1 to 16, one to four KV heads),
+head dim 64 or 128, the pool dtype, a chunking (the library's choice or an
+explicit multiple of 16 or 32), and, for some cases, blocks marked as not
+attended (negative table entries, the restricted decode of "Not all thinking
+needs HBM").  Output and lse must match the oracle's step over the attended
+tokens, to the tolerances of the other parity tests.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+CASES = 24
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import decode_attention_paged_04_amd as kvd
+    import gpu_harness as H
+    import workloads as W
+    return kvd, H, W, torch
+
+
+def _draw(seed):
+    rng = np.random.default_rng(seed)
+    b = int(rng.integers(1, 21))
+    lens = rng.integers(0, 700, b)
+    lens[rng.random(b) < 0.15] = 0
+    lens[rng.random(b) < 0.1] = 1
+    n_kv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
+    d = int(rng.choice([64, 128]))
+    fp8 = bool(rng.random() < 0.4)
+    chunk = int(rng.choice([0, 16, 32, 48, 96, 160, 512]))
+    drop = bool(rng.random() < 0.4)
+    return rng, lens.astype(np.int32), n_kv, g, d, fp8, chunk, drop
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_random_configuration(env, seed):
+    kvd, H, W, torch = env
+    from oracle import tiers
+    rng, lens, n_kv, g, d, fp8, chunk, drop = _draw(1000 + seed)
+    H.say(f"fuzz seed={seed}: b={len(lens)} n_kv={n_kv} g={g} d={d} fp8={fp8} chunk={chunk} drop={drop} "
+          f"max_len={int(lens.max())}")
+    w = W.DecodeWorkload(f"fuzz{seed}", seed=2000 + seed, b=len(lens), layers=1, n_q=g * n_kv, n_kv=n_kv,
+                         head_dim=d, ctx=("fixed", 0), kv_dtype="fp8" if fp8 else "bf16")
+    table, nb = W.block_tables(w, lens, pad_value=-1)
+    case = H.PagedCase(w, lens=lens, table=table, num_blocks=nb)
+    run_table = case.table.copy()
+    if drop:
+        for i, s in enumerate(lens):
+            for blk in range(-(-int(s) // 16)):
+                if rng.random() < 0.3:
+                    run_table[i, blk] = -1
+    out = torch.empty_like(case.q[0])
+    lse = torch.empty(case.q[0].shape[:2], dtype=torch.float32, device="cuda")
+    kvd.decode(case.pool, 0, case.q[0], torch.from_numpy(run_table).cuda(), case.lens_t, max(case.max_ctx, 1),
+               out=out, lse_out=lse, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    qf = H.bf16_to_f64(case.q[0])
+    ref_o = np.zeros(qf.shape)
+    ref_l = np.full(qf.shape[:2], -np.inf)
+    for i, s in enumerate(lens):
+        s = int(s)
+        if s == 0:
+            continue
+        K, V = case.logical(0, i)
+        keep = np.array([run_table[i, t // 16] >= 0 for t in range(s)], dtype=bool)
+        ref_o[i], ref_l[i] = tiers.restricted_decode(qf[i], K, V, keep)
+    H.assert_bf16_close(out, ref_o, what=f"fuzz seed {seed}")
+    H.assert_lse_close(lse, ref_l)
