@@ -49,7 +49,7 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
 INFINITY_CACHE_BYTES = 256 << 20
 HEADLINE = "8b_layer"
 SECONDARY = "70b_long"
-DECODE_SOURCES = ["decode.hip", "device_common.h", "kvd_internal.h"]
+DECODE_SOURCES = ["decode.hip", "device_common.h", "kv_store.h", "kvd_internal.h"]
 
 
 def log(msg: str):
@@ -247,7 +247,9 @@ class Workload:
         """Mean duration (s) of one kvd_write_kv call storing one token per
         sequence -- what a decode step writes per layer -- into each
         sequence's last block (a partly filled block re-quantises under FP8):
-        (eager calls from Python, calls replayed from a HIP graph)."""
+        (eager calls from Python, calls replayed from a HIP graph, the decode
+        call alone and the decode call with the append fused, both replayed
+        from graphs)."""
         torch, kvd, w = self.torch, self.kvd, self.w
         last = torch.from_numpy(self.table[np.arange(w.b), (self.lens - 1) // 16] * 16 + (self.lens - 1) % 16)
         slots = last.to(torch.int32).cuda()
@@ -284,7 +286,41 @@ class Workload:
             graph.replay()
         b.record(stream)
         torch.cuda.synchronize()
-        return eager, a.elapsed_time(b) / (reps * per_graph) / 1e3
+        graphed = a.elapsed_time(b) / (reps * per_graph) / 1e3
+
+        # the same appends fused into the decode calls (kvd_decode_attn_append),
+        # against the decode calls alone, both replayed from graphs
+        args = self.args[0][0]
+
+        def here():                           # the stream being captured, or the current one
+            return int(torch.cuda.current_stream().cuda_stream)
+
+        def decode_only():
+            self.call(0, 0, here())
+
+        def fused():
+            st = kvd.lib.kvd_decode_attn_append(self.pools[0].handle, 0, ctypes.byref(args), K.data_ptr(),
+                                                V.data_ptr(), here())
+            if st != 0:
+                raise RuntimeError(f"fused append failed: {kvd.kvd_status_string(st)}")
+
+        per_call = {}
+        for name, fn in (("decode", decode_only), ("fused", fused)):
+            fn()
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for _ in range(per_graph):
+                    fn()
+            gr.replay()
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(reps):
+                gr.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            per_call[name] = a.elapsed_time(b) / (reps * per_graph) / 1e3
+        return eager, graphed, per_call["decode"], per_call["fused"]
 
     def config(self):
         w = self.w
@@ -515,10 +551,11 @@ def mixed_entry(name: str, layers: int, steps: int, fp8_share: float = 0.5):
 def append_entry(name: str, calls: int):
     """Cost of the decode step's own write: one token per sequence per layer."""
     wl = Workload(name, 0, 1, layers=1)
-    eager, graphed = wl.time_append(calls)
+    eager, graphed, dec, fused = wl.time_append(calls)
     w = wl.w
     e = {"workload": f"{w.name} (1 layer)", "kv_dtype": w.kv_dtype, "tokens_per_call": w.b,
          "us_per_call": round(graphed * 1e6, 2), "us_per_call_eager": round(eager * 1e6, 2),
+         "decode_us": round(dec * 1e6, 2), "fused_append_decode_us": round(fused * 1e6, 2),
          "stored_bytes_per_call": w.b * 2 * w.n_kv * w.head_dim * wl.kv_bytes}
     wl.free()
     return e

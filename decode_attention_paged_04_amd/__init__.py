@@ -58,6 +58,8 @@ EXPORTS = {
     "kvd_decode_attn_fp8": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs), ctypes.c_void_p),
     "kvd_decode_attn_mixed": (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs),
                               ctypes.c_void_p),
+    "kvd_decode_attn_append": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs), ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_void_p),
     "kvd_decode_partials": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs), ctypes.c_void_p,
                             ctypes.c_void_p, ctypes.c_void_p),
     "kvd_merge_partials": (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -296,6 +298,18 @@ def kvd_decode_attn_fp8(pool: Pool, layer: int, args: DecodeArgs, stream=None):
            "kvd_decode_attn_fp8")
 
 
+def kvd_decode_attn_append(pool: Pool, layer: int, args: DecodeArgs, new_k, new_v, stream=None):
+    """Store token s_i - 1 of every sequence (bf16 ``new_k``/``new_v``
+    ``[b][n_kv][head_dim]``) and decode, in one launch (bf16 or FP8 pool)."""
+    import torch
+    shape = (int(args.b), pool.desc.n_kv, pool.desc.head_dim)
+    _check_tensor(new_k, "new_k", shape, torch.bfloat16)
+    _require(new_k.is_cuda, "new_k must be on the GPU")
+    _check_tensor(new_v, "new_v", shape, torch.bfloat16, new_k.device)
+    _check(lib.kvd_decode_attn_append(pool.handle, layer, ctypes.byref(args), _ptr(new_k), _ptr(new_v),
+                                      _stream(stream)), "kvd_decode_attn_append")
+
+
 def kvd_decode_attn_mixed(pool_bf16: Pool, pool_fp8: Pool, layer: int, args: DecodeArgs, stream=None):
     """Decode over bf16 blocks of ``pool_bf16`` and FP8 blocks of ``pool_fp8``
     (table entries of FP8 blocks carry bit 30; see kvd_mixed_row)."""
@@ -378,8 +392,9 @@ def kvd_debug_fp8_decode(codes, out, stream=None):
 
 def decode(pool: Pool, layer: int, q, block_table, context_lens, max_context_len: int, out=None,
            lse_out=None, chunk_tokens: int = 0, score=None, score_weight: float = 0.0,
-           workspace=None, stream=None):
-    """Convenience: allocate out/workspace as needed and run one decode call."""
+           workspace=None, stream=None, new_k=None, new_v=None):
+    """Convenience: allocate out/workspace as needed and run one decode call
+    (with ``new_k``/``new_v``: the fused append of token s_i - 1 first)."""
     import torch
     if out is None:
         out = torch.empty_like(q)
@@ -388,7 +403,11 @@ def decode(pool: Pool, layer: int, q, block_table, context_lens, max_context_len
     ws = workspace
     if ws is None:
         ws = allocate_workspace(pool, args, device=q.device)
-    (kvd_decode_attn_fp8 if pool.fp8 else kvd_decode_attn)(pool, layer, args, stream)
+    if new_k is not None or new_v is not None:
+        _require(new_k is not None and new_v is not None, "new_k and new_v go together")
+        kvd_decode_attn_append(pool, layer, args, new_k, new_v, stream)
+    else:
+        (kvd_decode_attn_fp8 if pool.fp8 else kvd_decode_attn)(pool, layer, args, stream)
     return out, ws
 
 

@@ -115,9 +115,11 @@ kvd_status plan_decode(const PoolView& p, const kvd_decode_args* a, DecodePlan* 
 // One decode call.  ext_part_o / ext_part_lse (both or neither): write the
 // per-chunk partials there and stop, instead of producing the merged output.
 // pool8 (mixed precision only): the FP8 pool beside the bf16 pool `pool`.
+// new_k / new_v (both or neither): the fused append of token s_i - 1.
 kvd_status decode_common(const kvd_pool* pool, int32_t layer, const kvd_decode_args* a,
                          void* stream, bool any_dtype, kvd_dtype want, float* ext_part_o,
-                         float* ext_part_lse, const kvd_pool* pool8 = nullptr) {
+                         float* ext_part_lse, const kvd_pool* pool8 = nullptr,
+                         const void* new_k = nullptr, const void* new_v = nullptr) {
   if (!pool || !a) return KVD_ERR_INVALID_ARG;
   const PoolView& p = pool->v;
   if (!any_dtype && p.dtype != want) return KVD_ERR_DTYPE;
@@ -148,6 +150,8 @@ kvd_status decode_common(const kvd_pool* pool, int32_t layer, const kvd_decode_a
   const bool final_direct = !external && pl.final_direct;
   kvd::DecodeLaunch L{};
   L.layer_base = p.kv_base + (size_t)layer * (size_t)p.layer_bytes;
+  L.new_k = static_cast<const uint16_t*>(new_k);
+  L.new_v = static_cast<const uint16_t*>(new_v);
   L.layer_bytes = (uint32_t)p.layer_bytes;
   L.layer_scales = p.scale_base ? p.scale_base + (size_t)layer * p.num_blocks * p.n_kv * 2 : nullptr;
   L.q = static_cast<const uint16_t*>(a->q);
@@ -292,6 +296,12 @@ kvd_status kvd_decode_attn_mixed(const kvd_pool* pool_bf16, const kvd_pool* pool
                                  const kvd_decode_args* args, void* hip_stream) {
   if (!pool_fp8) return KVD_ERR_INVALID_ARG;
   return decode_common(pool_bf16, layer, args, hip_stream, false, KVD_BF16, nullptr, nullptr, pool_fp8);
+}
+
+kvd_status kvd_decode_attn_append(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
+                                  const void* new_k, const void* new_v, void* hip_stream) {
+  if (!new_k || !new_v) return KVD_ERR_INVALID_ARG;
+  return decode_common(pool, layer, args, hip_stream, true, KVD_BF16, nullptr, nullptr, nullptr, new_k, new_v);
 }
 
 kvd_status kvd_decode_partials(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,

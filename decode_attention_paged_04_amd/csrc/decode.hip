@@ -33,6 +33,7 @@
 //     are 8 consecutive rows of block G/2 -- 16 contiguous bytes of one
 //     channel row of the channel-major V tile.
 #include "device_common.h"
+#include "kv_store.h"
 #include "kvd_internal.h"
 
 #include <math.h>
@@ -180,6 +181,43 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
     return;
   }
 
+  // Fused append: the workgroup whose chunk holds token s - 1 first stores that
+  // token's K and V rows of head j into the pool, exactly as the write kernel
+  // would, and then reads them back like every other row.  FP8: waves 0 and 1
+  // re-quantise the K and the V tile; the new scales are kept in registers for
+  // this block, because the scalar cache may hold the old ones.
+  int32_t app_pid = -1;
+  float app_sK = 0.f, app_sV = 0.f;
+  if constexpr (!MIX) {
+    if (a.new_k != nullptr && s > 0 && (s - 1) / a.chunk == c) {
+      const int tl = s - 1;
+      const int32_t pid = load_invariant(a.block_table + (size_t)i * a.max_blocks + tl / kBlock);
+      if (pid >= 0 && pid < a.num_blocks) {
+        const uint16_t* kr = a.new_k + ((size_t)i * a.n_kv + j) * D;
+        const uint16_t* vr = a.new_v + ((size_t)i * a.n_kv + j) * D;
+        constexpr uint32_t kTPB = 2u * kBlock * D * (KIND == kFp8 ? 1 : 2);
+        char* tp = const_cast<char*>(a.layer_base) + tile_pair_offset(pid, j, a.num_blocks, a.n_kv, kTPB);
+        if constexpr (KIND == kFp8) {
+          __shared__ float sh_app[2];
+          if (wave < 2) {
+            float* sc = const_cast<float*>(a.layer_scales) + ((size_t)j * a.num_blocks + pid) * 2 + wave;
+            const float v = fp8_store_rows<D>(reinterpret_cast<uint8_t*>(tp), sc, wave, tl % kBlock, 1,
+                                              wave ? vr : kr, 0, lane);
+            if (lane == 0) sh_app[wave] = v;
+          }
+          __syncthreads();
+          // uniform: keep them in scalar registers
+          app_sK = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sh_app[0])));
+          app_sV = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sh_app[1])));
+        } else {
+          if (wave == 0) bf16_store_row<D>(reinterpret_cast<uint16_t*>(tp), tl % kBlock, kr, vr, lane);
+          __syncthreads();
+        }
+        app_pid = pid;
+      }
+    }
+  }
+
   // q as the B operand of S = K q^T: column r16 = query head j*g + r16.
   bf16x8 qf[NC];
   {
@@ -261,10 +299,14 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
         // Head-major: this head's scales of all blocks are contiguous.
         const float* sc = (OTHER ? a.layer_scales8 : a.layer_scales) +
                           (size_t)j * (OTHER ? a.num_blocks8 : a.num_blocks) * 2;
-        const float sk0 = t0 == kOutOfRange ? 0.f : load_invariant(sc + (size_t)pid0 * 2 + 0);
-        const float sv0 = t0 == kOutOfRange ? 0.f : load_invariant(sc + (size_t)pid0 * 2 + 1);
-        const float sk1 = t1 == kOutOfRange ? 0.f : load_invariant(sc + (size_t)pid1 * 2 + 0);
-        const float sv1 = t1 == kOutOfRange ? 0.f : load_invariant(sc + (size_t)pid1 * 2 + 1);
+        float sk0 = t0 == kOutOfRange ? 0.f : load_invariant(sc + (size_t)pid0 * 2 + 0);
+        float sv0 = t0 == kOutOfRange ? 0.f : load_invariant(sc + (size_t)pid0 * 2 + 1);
+        float sk1 = t1 == kOutOfRange ? 0.f : load_invariant(sc + (size_t)pid1 * 2 + 0);
+        float sv1 = t1 == kOutOfRange ? 0.f : load_invariant(sc + (size_t)pid1 * 2 + 1);
+        if constexpr (!MIX) {
+          if (pid0 == app_pid) { sk0 = app_sK; sv0 = app_sV; }   // the block this call appended to
+          if (pid1 == app_pid) { sk1 = app_sK; sv1 = app_sV; }
+        }
         f.sK = G < 2 ? sk0 : sk1;
         f.sV = G < 2 ? sv0 : sv1;
       }

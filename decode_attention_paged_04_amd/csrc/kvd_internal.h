@@ -59,6 +59,10 @@ struct DecodeLaunch {
   uint32_t layer_bytes8;
   const float* layer_scales8;
   int32_t num_blocks8;
+  // fused append (or null): bf16 [b][n_kv][D] K and V of token s_i - 1, stored
+  // before attention by the workgroup whose chunk holds that token
+  const uint16_t* new_k;
+  const uint16_t* new_v;
 };
 
 hipError_t launch_decode(const DecodeLaunch& a, int head_dim, int kind, bool final_direct,

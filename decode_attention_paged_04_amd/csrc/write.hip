@@ -1,6 +1,7 @@
 // Storing new tokens into the pool (bf16 copy, FP8 E4M3 quantisation) and the
 // test hooks that expose the decode kernels' addressing and FP8 widening.
 #include "device_common.h"
+#include "kv_store.h"
 #include "kvd_internal.h"
 
 #include <math.h>
@@ -31,33 +32,6 @@ __global__ __launch_bounds__(256) void write_bf16_kernel(char* __restrict__ laye
   tile[v_elem(row, ch, D)] = v[e];
 }
 
-// Nearest-even E4M3FN code of y, saturating at +-448 (sign kept, -0 -> 0x80).
-__device__ inline uint32_t e4m3_encode(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fabsf(y);
-  uint32_t code;
-  if (!(a < 448.0f)) {
-    code = 0x7Eu;
-  } else if (a < 0.015625f) {                       // below 2^-6: grid of m * 2^-9
-    code = (uint32_t)rintf(a * 512.0f);             // exact scaling; rint ties to even
-  } else {
-    const uint32_t ab = __float_as_uint(a);
-    const uint32_t e = (ab >> 23) - 127u + 7u;      // biased E4M3 exponent, 1..15
-    const uint32_t mant = ab & 0x7FFFFFu;
-    uint32_t q = (e << 3) | (mant >> 20);
-    const uint32_t rem = mant & 0xFFFFFu;
-    q += (rem > 0x80000u) || (rem == 0x80000u && (q & 1u));   // carry may bump the exponent
-    code = q;
-  }
-  return sign | code;
-}
-
-// Widen one E4M3FN code to fp32 with the conversion the decode kernels use
-// (exact: every E4M3FN value is a bf16 value).
-__device__ inline float e4m3_to_float(uint32_t code) {
-  return (float)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, false)[0];
-}
-
 // One wave per (run, KV head, K|V).  A run is a maximal stretch of entries of
 // the slot mapping that fill consecutive rows r0, r0+1, ... of one block; rows
 // below r0 already hold codes under the tile's current scale.  The tile keeps
@@ -65,9 +39,8 @@ __device__ inline float e4m3_to_float(uint32_t code) {
 // scale, fp32) and the run's new rows.  Old codes are re-encoded from their
 // read-back values only if the scale changed; new rows are encoded under the
 // new scale.  A run starting at row 0 is the plain block quantisation.
-// Every load is issued before any is used (the slots around the entry, the old
-// scale, the old codes and the new rows), so a decode step's append costs about
-// two memory round trips: the loads, then the stores.
+// The slots around the entry are read with one vector load; the tile is then
+// stored by fp8_store_rows.
 template <int D>
 __global__ __launch_bounds__(64) void write_fp8_kernel(char* __restrict__ layer_base,
                                                        float* __restrict__ layer_scales,
@@ -76,7 +49,6 @@ __global__ __launch_bounds__(64) void write_fp8_kernel(char* __restrict__ layer_
                                                        const uint16_t* __restrict__ v,
                                                        const int32_t* __restrict__ slots,
                                                        int32_t n_tok) {
-  constexpr int CPL = D / 64;                       // channels per lane: lane, lane + 64
   const int t = blockIdx.x;
   const int j = blockIdx.y;
   const int which = blockIdx.z;                     // 0: K, 1: V
@@ -95,50 +67,9 @@ __global__ __launch_bounds__(64) void write_fp8_kernel(char* __restrict__ layer_
   const int n = 1 + __builtin_ctzll(~cont);
 
   const uint16_t* src = (which ? v : k) + ((size_t)t * n_kv + j) * D;
-  const size_t row_stride = (size_t)n_kv * D;
   uint8_t* tile = reinterpret_cast<uint8_t*>(layer_base + ((size_t)p * n_kv + j) * (2 * kBlock * D));
   float* scale_at = layer_scales + ((size_t)j * num_blocks + p) * 2 + which;   // head-major
-  auto at = [&](int r, int ch) -> uint8_t& { return tile[which ? v_elem(r, ch, D) : k_elem(r, ch, D, 1)]; };
-
-  const float s_old = r0 > 0 ? *scale_at : 0.f;
-  uint32_t old[kBlock][CPL];
-  float fresh[kBlock][CPL];
-#pragma unroll
-  for (int r = 0; r < kBlock; ++r) {
-#pragma unroll
-    for (int q = 0; q < CPL; ++q) {
-      const int ch = lane + 64 * q;
-      old[r][q] = r < r0 ? (uint32_t)at(r, ch) : 0u;
-      fresh[r][q] = r < n ? bf16_bits_to_float(src[r * row_stride + ch]) : 0.f;
-    }
-  }
-  float am = 0.f;
-#pragma unroll
-  for (int r = 0; r < kBlock; ++r) {
-#pragma unroll
-    for (int q = 0; q < CPL; ++q) {
-      if (r < r0) am = fmaxf(am, fabsf(e4m3_to_float(old[r][q]) * s_old));
-      if (r < n) am = fmaxf(am, fabsf(fresh[r][q]));
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
-  const float scale = am / 448.0f;
-
-  const bool reencode = r0 > 0 && scale != s_old;
-#pragma unroll
-  for (int r = 0; r < kBlock; ++r) {
-#pragma unroll
-    for (int q = 0; q < CPL; ++q) {
-      const int ch = lane + 64 * q;
-      if (reencode && r < r0) {
-        const float x = e4m3_to_float(old[r][q]) * s_old;
-        at(r, ch) = (uint8_t)(scale == 0.f ? 0u : e4m3_encode(x / scale));
-      }
-      if (r < n) at(r0 + r, ch) = (uint8_t)(scale == 0.f ? 0u : e4m3_encode(fresh[r][q] / scale));
-    }
-  }
-  if (lane == 0) *scale_at = scale;
+  fp8_store_rows<D>(tile, scale_at, which, r0, n, src, (size_t)n_kv * D, lane);
 }
 
 hipError_t launch_write(const PoolView& pv, int32_t layer, const uint16_t* k, const uint16_t* v,

@@ -200,6 +200,25 @@ kvd_status kvd_decode_attn(const kvd_pool* pool, int32_t layer, const kvd_decode
 kvd_status kvd_decode_attn_fp8(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
                                void* hip_stream);
 
+/* A decode step that first stores the step's own token, in one launch.  The
+ * token being decoded is already part of its context (s_i counts it) and its
+ * K/V go into the sequence's last block (froggydisk, section "KV 캐시를
+ * 줄이는 기법", the PagedAttention paragraph: the decode step writes into
+ * the partly filled last block).  new_k, new_v: device bf16 [b][n_kv][d_h],
+ * the K and V of token s_i - 1 of each sequence.  The call stores them at that
+ * token's slot -- block_table[i][(s_i - 1) / 16], row (s_i - 1) % 16 -- with
+ * the bytes kvd_write_kv would store (FP8: the tile re-quantised under
+ * kvd_write_kv's append rule), then runs the step of kvd_decode_attn
+ * (bf16 pool) or kvd_decode_attn_fp8 (FP8 pool) over the context including
+ * that token: outputs, lse, score and pool contents equal those of
+ * kvd_write_kv followed by the decode call, bit for bit.  The store is done by
+ * the workgroups whose chunk holds token s_i - 1, before they read that block.
+ * Nothing is stored for a sequence with s_i = 0 or whose last table entry is
+ * negative or >= num_blocks.  Args, workspace and errors as kvd_decode_attn;
+ * KVD_ERR_INVALID_ARG if new_k or new_v is NULL. */
+kvd_status kvd_decode_attn_append(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
+                                  const void* new_k, const void* new_v, void* hip_stream);
+
 /* Decode over a mixed-precision block set: bf16 blocks in pool_bf16 and FP8
  * E4M3 blocks in pool_fp8 (both with the same num_layers, n_kv, head_dim;
  * fewer than 2^30 blocks each), following "The KV Cache Is the New Memory
