@@ -238,3 +238,14 @@ def test_mixed_decode_errors():
     assert f(p16.handle, _pool(kvd.KVD_FP8_E4M3, n_kv=4).handle, 0, ctypes.byref(a), None) == 1
     assert f(p16.handle, None, 0, ctypes.byref(a), None) == 1
     assert f(p16.handle, p8.handle, 5, ctypes.byref(a), None) == 1         # layer out of range
+
+
+def test_fused_append_errors():
+    p16, p8 = _pool(), _pool(kvd.KVD_FP8_E4M3)
+    a = _args()
+    f = kvd.lib.kvd_decode_attn_append
+    assert f(p16.handle, 0, ctypes.byref(a), None, FAKE, None) == 1        # new_k missing
+    assert f(p8.handle, 0, ctypes.byref(a), FAKE, None, None) == 1         # new_v missing
+    assert f(None, 0, ctypes.byref(a), FAKE, FAKE, None) == 1
+    assert f(p16.handle, 5, ctypes.byref(a), FAKE, FAKE, None) == 1        # layer out of range
+    assert f(p16.handle, 0, ctypes.byref(_args(chunk_tokens=8)), FAKE, FAKE, None) == 1
