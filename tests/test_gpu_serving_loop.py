@@ -3,8 +3,9 @@
 The native block manager hands out blocks (prefix cache on: several requests
 share a system prompt's blocks), kvd_write_kv stores each prompt's uncached
 tokens and then one token per request per step, and kvd_decode_attn(_fp8)
-runs on the manager's block tables.  Requests finish and new ones arrive
-mid-loop and pick up the cached prefix.  The oracle keeps its own copy of
+runs on the manager's block tables -- or, in the fused variant, each step's
+token is stored by the decode launch itself (kvd_decode_attn_append).
+Requests finish and new ones arrive mid-loop and pick up the cached prefix.  The oracle keeps its own copy of
 every physical block (bf16 values, or FP8 codes and scales advanced with its
 append step) and computes each request's attention from the blocks its table
 names.
@@ -87,8 +88,9 @@ class PhysicalPool:
         return np.stack(Ks), np.stack(Vs)
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("fp8", [False, True])
-def test_decode_loop_with_shared_prefix(env, fp8):
+def test_decode_loop_with_shared_prefix(env, fp8, fused):
     kvd, H, torch = env
     from oracle import attention
     d = 128
@@ -144,16 +146,24 @@ def test_decode_loop_with_shared_prefix(env, fp8):
         slots = []
         for sid in sids:
             slots += bm.append(sid, 1, [int(rng.integers(0, 1000))])
-        write(slots, rng.standard_normal((len(sids), N_KV, d)).astype(np.float32) * (1 + step % 3),
-              rng.standard_normal((len(sids), N_KV, d)).astype(np.float32))
+        newk = rng.standard_normal((len(sids), N_KV, d)).astype(np.float32) * (1 + step % 3)
+        newv = rng.standard_normal((len(sids), N_KV, d)).astype(np.float32)
+        if fused:
+            newk, newv = as_stored(newk), as_stored(newv)
+            ref.write(slots, newk, newv)                 # the decode launch stores them on the GPU
+            new_k, new_v = bf16(newk).cuda(), bf16(newv).cuda()
+        else:
+            write(slots, newk, newv)
+            new_k = new_v = None
         max_blocks = max(-(-bm.length(s) // 16) for s in sids)
         table, lens = bm.fill_tables(sids, max_blocks)
+        assert all(int(table[i, (lens[i] - 1) // 16]) * 16 + (lens[i] - 1) % 16 == slots[i] for i in range(len(sids)))
         q = torch.randn((len(sids), N_KV * G, d), generator=torch.Generator().manual_seed(step)).to(torch.bfloat16)
         out = torch.empty_like(q).cuda()
         lse = torch.empty((len(sids), N_KV * G), dtype=torch.float32, device="cuda")
-        H.say(f"fp8={fp8} step {step}: {len(sids)} requests, lens {lens.tolist()}")
+        H.say(f"fp8={fp8} fused={fused} step {step}: {len(sids)} requests, lens {lens.tolist()}")
         kvd.decode(pool, 0, q.cuda(), torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda(),
-                   int(lens.max()), out=out, lse_out=lse)
+                   int(lens.max()), out=out, lse_out=lse, new_k=new_k, new_v=new_v)
         torch.cuda.synchronize()
         qf = H.bf16_to_f64(q)
         ref_o = np.zeros(qf.shape)
