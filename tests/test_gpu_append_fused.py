@@ -13,7 +13,7 @@ import pytest
 
 pytestmark = pytest.mark.gpu
 
-LENS = [0, 1, 16, 17, 33, 47, 48, 100, 257]
+LENS = [0, 1, 16, 17, 33, 47, 48, 100, 257, 49, 96, 97]
 
 
 @pytest.fixture(scope="module")
