@@ -89,7 +89,9 @@ kvd_status plan_decode(const PoolView& p, const kvd_decode_args* a, DecodePlan* 
   if (chunk > whole) chunk = whole;
   pl.chunk = (int32_t)chunk;
   pl.n_chunks = (int32_t)std::max<int64_t>(1, (pl.ctx_bound + chunk - 1) / chunk);
-  if ((int64_t)pl.n_chunks * std::max(a->b, 1) * p.n_kv >= ((int64_t)1 << 31)) return KVD_ERR_UNSUPPORTED;
+  // grids of 256-work-item workgroups: fewer than 2^32 work-items per launch
+  if ((int64_t)pl.n_chunks * std::max(a->b, 1) * p.n_kv >= ((int64_t)1 << 24)) return KVD_ERR_UNSUPPORTED;
+  if ((int64_t)a->b * a->n_q >= ((int64_t)1 << 24)) return KVD_ERR_UNSUPPORTED;
   pl.final_direct = pl.n_chunks == 1;
   pl.scores = a->score != nullptr;
   pl.logit_stride = (pl.ctx_bound + 31) / 32 * 32 + 32;
@@ -256,7 +258,8 @@ kvd_status kvd_write_kv(const kvd_pool* pool, int32_t layer, const void* k, cons
   if (layer < 0 || layer >= pool->v.num_layers || n_tok < 0) return KVD_ERR_INVALID_ARG;
   if (n_tok == 0) return KVD_OK;
   if (!k || !v || !slot_mapping) return KVD_ERR_INVALID_ARG;
-  if ((int64_t)n_tok * pool->v.n_kv * pool->v.head_dim >= ((int64_t)1 << 40)) return KVD_ERR_UNSUPPORTED;
+  // the bf16 store runs one work-item per element: fewer than 2^32 per launch
+  if ((int64_t)n_tok * pool->v.n_kv * pool->v.head_dim >= ((int64_t)1 << 32)) return KVD_ERR_UNSUPPORTED;
   clear_stale_error();
   KVD_TRY_HIP(kvd::launch_write(pool->v, layer, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                         slot_mapping, n_tok, static_cast<hipStream_t>(hip_stream)));
@@ -317,7 +320,7 @@ kvd_status kvd_merge_partials(const float* part_o, const float* part_lse, int32_
   if (d_h != 64 && d_h != 128) return KVD_ERR_UNSUPPORTED;
   if (b == 0) return KVD_OK;
   if (!part_o || !part_lse || !out_bf16) return KVD_ERR_INVALID_ARG;
-  if ((int64_t)b * n_q >= ((int64_t)1 << 31)) return KVD_ERR_UNSUPPORTED;
+  if ((int64_t)b * n_q >= ((int64_t)1 << 24)) return KVD_ERR_UNSUPPORTED;   // 256-work-item workgroups
   clear_stale_error();
   KVD_TRY_HIP(kvd::launch_merge(part_o, part_lse, b, n_q, n_chunks, d_h, static_cast<uint16_t*>(out_bf16),
                                 lse_out, nullptr, static_cast<hipStream_t>(hip_stream)));

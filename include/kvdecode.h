@@ -128,7 +128,9 @@ kvd_status kvd_destroy_pool(kvd_pool* pool);
  *   Within one call a block may receive at most one run; two runs into one
  *   block in the same call race (undefined result).
  *   Rows of a block past the last one written keep whatever they held and are
- *   never read as long as the context lengths exclude them. */
+ *   never read as long as the context lengths exclude them.
+ * bf16 pools: n_tok * n_kv * head_dim must stay below 2^32 (one work-item per
+ * element), else KVD_ERR_UNSUPPORTED. */
 kvd_status kvd_write_kv(const kvd_pool* pool, int32_t layer, const void* k, const void* v,
                         const int32_t* slot_mapping, int32_t n_tok, void* hip_stream);
 
@@ -164,7 +166,10 @@ typedef struct {
 } kvd_decode_args;
 
 /* How a decode call splits the context: chunk length in tokens and number of
- * chunks.  Pure host function of the pool and the arguments. */
+ * chunks.  Pure host function of the pool and the arguments.  A launch holds
+ * fewer than 2^32 work-items and a workgroup 256, so b * n_kv * n_chunks and
+ * b * n_q must stay below 2^24 (KVD_ERR_UNSUPPORTED otherwise, from every
+ * decode entry point). */
 kvd_status kvd_decode_plan(const kvd_pool* pool, const kvd_decode_args* args,
                            int32_t* chunk_tokens, int32_t* n_chunks);
 

@@ -249,3 +249,18 @@ def test_fused_append_errors():
     assert f(None, 0, ctypes.byref(a), FAKE, FAKE, None) == 1
     assert f(p16.handle, 5, ctypes.byref(a), FAKE, FAKE, None) == 1        # layer out of range
     assert f(p16.handle, 0, ctypes.byref(_args(chunk_tokens=8)), FAKE, FAKE, None) == 1
+
+
+def test_launch_size_limits():
+    """Grids of 256-work-item workgroups hold fewer than 2^32 work-items."""
+    pool = _pool()                                   # n_kv = 2, d_h = 128
+    big = _args(b=1 << 20, max_context_len=128, max_blocks_per_seq=8, chunk_tokens=16,
+                workspace=FAKE, workspace_bytes=1 << 62)
+    assert _status("kvd_decode_attn", pool.handle, 0, ctypes.byref(big), None) == 2    # 2^24 workgroups
+    ok = _args(b=(1 << 20) - 1, max_context_len=128, max_blocks_per_seq=8, chunk_tokens=16)
+    c, n = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert _status("kvd_decode_plan", pool.handle, ctypes.byref(ok), ctypes.byref(c), ctypes.byref(n)) == 0
+    heads = _args(b=1 << 21, max_context_len=16, max_blocks_per_seq=1)              # b * n_q = 2^24
+    assert _status("kvd_decode_attn", pool.handle, 0, ctypes.byref(heads), None) == 2
+    assert _status("kvd_write_kv", pool.handle, 0, FAKE, FAKE, FAKE, 1 << 24, None) == 2   # 2^32 elements
+    assert _status("kvd_merge_partials", FAKE, FAKE, 1 << 21, 8, 4, 128, FAKE, None, None) == 2
