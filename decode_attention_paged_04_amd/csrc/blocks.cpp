@@ -26,6 +26,9 @@ struct Key {
   }
 };
 
+// The SplitMix64 output function (Steele, Lea and Flood, "Fast splittable
+// pseudorandom number generators", OOPSLA 2014; the published constants):
+// a bijective 64-bit mix.
 inline uint64_t mix64(uint64_t x) {
   x ^= x >> 30;
   x *= 0xBF58476D1CE4E5B9ull;
