@@ -4,6 +4,7 @@
 // full precision before attention) and T3 (evicted); attention covers T0 and
 // T1, expressed as a block-table row whose evicted entries are negative.
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <numeric>
@@ -61,10 +62,9 @@ kvd_status kvd_tier_plan(const double* block_scores, int32_t n_blocks, int32_t p
 kvd_status kvd_tier_restrict(const int32_t* table_row, const int8_t* tiers, int32_t n_blocks,
                              int32_t* out_row) {
   if (n_blocks < 0 || (n_blocks > 0 && (!table_row || !tiers || !out_row))) return KVD_ERR_INVALID_ARG;
-  for (int32_t b = 0; b < n_blocks; ++b) {
+  for (int32_t b = 0; b < n_blocks; ++b)        // check everything before writing (in place allowed)
     if (tiers[b] != KVD_TIER_T0 && tiers[b] != KVD_TIER_T1 && tiers[b] != KVD_TIER_T3) return KVD_ERR_INVALID_ARG;
-    out_row[b] = tiers[b] == KVD_TIER_T3 ? -1 : table_row[b];
-  }
+  for (int32_t b = 0; b < n_blocks; ++b) out_row[b] = tiers[b] == KVD_TIER_T3 ? -1 : table_row[b];
   return KVD_OK;
 }
 
@@ -85,6 +85,7 @@ extern "C" kvd_status kvd_mixed_row(const int32_t* ids_bf16, int32_t n_bf16, con
   const int32_t tf = fp8_last ? 0 : kBit, ts = fp8_last ? kBit : 0;
   const int32_t pad = (ns > 0 && nf % 2) ? 1 : 0;
   const int64_t n = (int64_t)nf + pad + ns;
+  if (n > INT32_MAX - 1) return KVD_ERR_INVALID_ARG;
   *n_entries = (int32_t)n;
   *context_len = 0;
   if (n == 0) return KVD_OK;
