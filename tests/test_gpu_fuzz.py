@@ -6,7 +6,8 @@ head dim 64 or 128, the pool dtype, a chunking (the library's choice or an
 explicit multiple of 16 or 32), and, for some cases, blocks marked as not
 attended (negative table entries, the restricted decode of "Not all thinking
 needs HBM").  Output and lse must match the oracle's step over the attended
-tokens, to the tolerances of the other parity tests.
+tokens, to the tolerances of the other parity tests; a second set of draws
+adds the fused cumulative score and checks its update as well.
 """
 import numpy as np
 import pytest
@@ -75,3 +76,49 @@ def test_random_configuration(env, seed):
         ref_o[i], ref_l[i] = tiers.restricted_decode(qf[i], K, V, keep)
     H.assert_bf16_close(out, ref_o, what=f"fuzz seed {seed}")
     H.assert_lse_close(lse, ref_l)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_configuration_with_scores(env, seed):
+    """The same kind of draw with a fused cumulative score (chunks of whole
+    32-token pairs): output and the score update against the oracle."""
+    kvd, H, W, torch = env
+    from oracle import scores, tiers
+    rng, lens, n_kv, g, d, fp8, _, drop = _draw(3000 + seed)
+    chunk = int(rng.choice([0, 32, 96, 160, 512]))
+    weight = float(rng.choice([1.0, 0.25, 1.0 / 32]))
+    H.say(f"fuzz+scores seed={seed}: b={len(lens)} n_kv={n_kv} g={g} d={d} fp8={fp8} chunk={chunk} "
+          f"drop={drop} weight={weight}")
+    w = W.DecodeWorkload(f"fuzzs{seed}", seed=4000 + seed, b=len(lens), layers=1, n_q=g * n_kv, n_kv=n_kv,
+                         head_dim=d, ctx=("fixed", 0), kv_dtype="fp8" if fp8 else "bf16")
+    table, nb = W.block_tables(w, lens, pad_value=-1)
+    case = H.PagedCase(w, lens=lens, table=table, num_blocks=nb)
+    run_table = case.table.copy()
+    if drop:
+        for i, s in enumerate(lens):
+            for blk in range(-(-int(s) // 16)):
+                if rng.random() < 0.3:
+                    run_table[i, blk] = -1
+    stride = max(case.max_ctx, 1) + int(rng.integers(0, 9))
+    init = rng.random((len(lens), stride)).astype(np.float32)
+    score = torch.from_numpy(init).cuda()
+    out = torch.empty_like(case.q[0])
+    kvd.decode(case.pool, 0, case.q[0], torch.from_numpy(run_table).cuda(), case.lens_t, max(case.max_ctx, 1),
+               out=out, chunk_tokens=chunk, score=score, score_weight=weight)
+    torch.cuda.synchronize()
+    qf = H.bf16_to_f64(case.q[0])
+    ref_o = np.zeros(qf.shape)
+    ref_s = init.astype(np.float64).copy()
+    for i, s in enumerate(lens):
+        s = int(s)
+        if s == 0:
+            continue
+        K, V = case.logical(0, i)
+        keep = np.array([run_table[i, t // 16] >= 0 for t in range(s)], dtype=bool)
+        ref_o[i], _ = tiers.restricted_decode(qf[i], K, V, keep)
+        ref_s[i, :s] += scores.layer_increment(tiers.restricted_weights(qf[i], K, keep), weight)
+    H.assert_bf16_close(out, ref_o, what=f"fuzz+scores seed {seed}")
+    got = score.cpu().double().numpy()
+    assert np.all(np.isfinite(got))
+    err = H.score_rel_error(got, ref_s)
+    assert err <= H.TOL_SCORE_REL, err
