@@ -122,3 +122,82 @@ def test_random_configuration_with_scores(env, seed):
     assert np.all(np.isfinite(got))
     err = H.score_rel_error(got, ref_s)
     assert err <= H.TOL_SCORE_REL, err
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_mixed_precision(env, seed):
+    """Random draws for kvd_decode_attn_mixed: each block of each sequence
+    in the bf16 or the FP8 pool at random, rows built by kvd_mixed_row, random
+    chunking; output and lse against the oracle's step over the stored blocks."""
+    kvd, H, W, torch = env
+    from oracle import e4m3, mixed
+    rng = np.random.default_rng(5000 + seed)
+    b = int(rng.integers(1, 12))
+    lens = rng.integers(0, 400, b)
+    lens[rng.random(b) < 0.15] = 0
+    n_kv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    chunk = int(rng.choice([0, 16, 48, 160]))
+    p_fp8 = float(rng.random())
+    H.say(f"mixed fuzz seed={seed}: b={b} n_kv={n_kv} g={g} d={d} chunk={chunk} p_fp8={p_fp8:.2f}")
+    tg = torch.Generator().manual_seed(6000 + seed)
+    K = [torch.randn((int(s), n_kv, d), generator=tg).to(torch.bfloat16) for s in lens]
+    V = [torch.randn((int(s), n_kv, d), generator=tg).to(torch.bfloat16) for s in lens]
+    q = torch.randn((b, n_kv * g, d), generator=tg).to(torch.bfloat16)
+    prec = [list((rng.random(-(-int(s) // 16)) < p_fp8).astype(int)) for s in lens]
+    n16 = sum(p.count(0) for p in prec) + 2
+    n8 = sum(p.count(1) for p in prec) + 2
+    pools = (kvd.allocate_pool(1, n16, n_kv, d, kvd.KVD_BF16), kvd.allocate_pool(1, n8, n_kv, d, kvd.KVD_FP8_E4M3))
+    for p in pools:
+        p.kv.fill_(0xFF)
+    perm = (list(rng.permutation(n16)), list(rng.permutation(n8)))
+    phys = {}
+    for which in (0, 1):
+        Ks, Vs, slots = [], [], []
+        for i, s in enumerate(lens):
+            for blk, pr in enumerate(prec[i]):
+                if pr != which:
+                    continue
+                phys[(i, blk)] = int(perm[which].pop())
+                lo, hi = 16 * blk, min(int(s), 16 * blk + 16)
+                Ks.append(K[i][lo:hi])
+                Vs.append(V[i][lo:hi])
+                slots += [phys[(i, blk)] * 16 + r for r in range(hi - lo)]
+        if slots:
+            kvd.kvd_write_kv(pools[which], 0, torch.cat(Ks).cuda(), torch.cat(Vs).cuda(),
+                             torch.tensor(slots, dtype=torch.int32, device="cuda"))
+    rows, ctx = [], []
+    for i, s in enumerate(lens):
+        nb = len(prec[i])
+        ids16 = [phys[(i, k)] for k in range(nb) if not prec[i][k]]
+        ids8 = [phys[(i, k)] for k in range(nb) if prec[i][k]]
+        row, c = kvd.mixed_row(ids16, ids8, bool(prec[i][-1]) if nb else True, int(s) - 16 * (nb - 1) if nb else 16)
+        rows.append(row)
+        ctx.append(c)
+    mb = max(max(len(r) for r in rows), 1)
+    table = np.full((b, mb), -1, dtype=np.int32)
+    for i, r in enumerate(rows):
+        table[i, :len(r)] = r
+    out = torch.empty_like(q).cuda()
+    lse = torch.empty((b, n_kv * g), dtype=torch.float32, device="cuda")
+    kvd.decode_mixed(pools[0], pools[1], 0, q.cuda(), torch.from_numpy(table).cuda(),
+                     torch.tensor(ctx, dtype=torch.int32, device="cuda"), max(max(ctx), 1), out=out, lse_out=lse,
+                     chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    qf = H.bf16_to_f64(q)
+    ref_o = np.zeros(qf.shape)
+    ref_l = np.full(qf.shape[:2], -np.inf)
+    for i, s in enumerate(lens):
+        blocks = []
+        for blk, pr in enumerate(prec[i]):
+            lo, hi = 16 * blk, min(int(s), 16 * blk + 16)
+            Kb, Vb = H.bf16_to_f64(K[i][lo:hi]), H.bf16_to_f64(V[i][lo:hi])
+            if pr:
+                ck, sk = e4m3.quantize_sequence(Kb.astype(np.float32))
+                cv, sv = e4m3.quantize_sequence(Vb.astype(np.float32))
+                Kb, Vb = e4m3.dequantize_sequence(ck, sk), e4m3.dequantize_sequence(cv, sv)
+            blocks.append((Kb, Vb))
+        ref_o[i], ref_l[i] = mixed.decode_mixed(qf[i], blocks)
+    H.assert_bf16_close(out, ref_o, what=f"mixed fuzz seed {seed}")
+    H.assert_lse_close(lse, ref_l)
