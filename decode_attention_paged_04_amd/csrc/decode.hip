@@ -243,8 +243,8 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
 
   const int npairs = (ntok + 31) >> 5;
 
-  // One pass over this wave's pairs, all of precision F8.
-  auto run = [&](auto f8tag) {
+  // One pass over this wave's pairs in [p0, p1), all of precision F8.
+  auto run = [&](auto f8tag, int p0, int p1) {
     constexpr bool F8 = decltype(f8tag)::value;
     using R = PairRegs<D, F8>;
     constexpr int EE = R::E;                           // bytes per element
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
     // touching memory, and the number of loads in flight stays the same on every
     // path, so the waits before each use cover exactly the pair being used.
     auto issue = [&](R& f, int p) {
-      const bool live = p < npairs;
+      const bool live = p < p1;
       const int nvalid = min(32, ntok - (p << 5));
       int32_t pid0 = live ? load_invariant(bt + 2 * p) : -1;
       int32_t pid1 = live && nvalid > kBlock ? load_invariant(bt + 2 * p + 1) : -1;
@@ -442,13 +442,13 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
     };
 
     // Two register sets: the next pair's loads are in flight while the current
-    // pair is consumed.  This wave owns pairs wave, wave + kWaves, ...; they are
-    // taken two at a time so that every pass through the loop has the same
-    // loads outstanding (a load past the end is an out-of-range no-op).
-    const int nmine = npairs > wave ? (npairs - wave + kWaves - 1) / kWaves : 0;
+    // pair is consumed.  This wave owns pairs p0 + wave, p0 + wave + kWaves, ...;
+    // they are taken two at a time so that every pass through the loop has the
+    // same loads outstanding (a load past the end is an out-of-range no-op).
+    const int nmine = p1 - p0 > wave ? (p1 - p0 - wave + kWaves - 1) / kWaves : 0;
     if (nmine > 0) {
       R fa, fb;
-      int p = wave;
+      int p = p0 + wave;
       issue(fa, p);
       int k = 0;
       for (; k + 1 < nmine; k += 2) {
@@ -462,10 +462,36 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
     }
   };
   if constexpr (MIX) {
-    run(std::false_type{});
-    run(std::true_type{});
+    // Each pass visits only the span of pairs that hold a block of its
+    // precision.  A row lists one precision's pages before the other's, so the
+    // two spans meet rather than overlap; any other row is still right, the
+    // spans then overlap and each pass skips the other precision's blocks.
+    // Lane l reads the entries of pair g0 + l; ballots give the first and last
+    // pair of each precision.
+    int lo16 = npairs, hi16 = 0, lo8 = npairs, hi8 = 0;
+    for (int g0 = 0; g0 < npairs; g0 += 64) {
+      const int p = g0 + lane;
+      bool has16 = false, has8 = false;
+      if (p < npairs) {
+        const int32_t e0 = bt[2 * p];
+        const int32_t e1 = ntok - (p << 5) > kBlock ? bt[2 * p + 1] : -1;
+        has16 = (e0 >= 0 && !(e0 & kPrecisionBit)) || (e1 >= 0 && !(e1 & kPrecisionBit));
+        has8 = (e0 >= 0 && (e0 & kPrecisionBit)) || (e1 >= 0 && (e1 & kPrecisionBit));
+      }
+      const uint64_t m16 = __ballot(has16), m8 = __ballot(has8);
+      if (m16) {
+        lo16 = min(lo16, g0 + (int)__builtin_ctzll(m16));
+        hi16 = g0 + 64 - (int)__builtin_clzll(m16);
+      }
+      if (m8) {
+        lo8 = min(lo8, g0 + (int)__builtin_ctzll(m8));
+        hi8 = g0 + 64 - (int)__builtin_clzll(m8);
+      }
+    }
+    run(std::false_type{}, __builtin_amdgcn_readfirstlane(lo16), __builtin_amdgcn_readfirstlane(max(lo16, hi16)));
+    run(std::true_type{}, __builtin_amdgcn_readfirstlane(lo8), __builtin_amdgcn_readfirstlane(max(lo8, hi8)));
   } else {
-    run(std::integral_constant<bool, KIND == kFp8>{});
+    run(std::integral_constant<bool, KIND == kFp8>{}, 0, npairs);
   }
 
   // Whole-head sum of this wave.

@@ -232,11 +232,12 @@ kvd_status kvd_decode_attn_append(const kvd_pool* pool, int32_t layer, const kvd
  * pages read in one header-guided pass).  Each block_table entry names its
  * block's pool in bit 30 (set: pool_fp8, block = entry & ~(1 << 30)) -- the
  * page header; a negative entry is a block that is not attended.  Entries
- * 2k and 2k+1 of a row form a page that must hold one precision (pad with -1:
- * a row lists one precision's blocks, a -1 if that run is odd, then the
- * other's); a page mixing the two reads garbage (never out of bounds).  Only
- * the final entry of a row may be partly filled.  The softmax covers the row's
- * blocks whatever their order, so the output is the step over those tokens.
+ * may come in any order, precisions alternating or not; a row that lists one
+ * precision's blocks, a -1 if that run is odd, then the other's
+ * (kvd_mixed_row) keeps pages of two entries tier-homogeneous, and each
+ * precision's pass then visits only its own span of the row.  Only the final
+ * entry of a row may be partly filled.  The softmax covers the row's blocks
+ * whatever their order, so the output is the step over those tokens.
  * No fused score (KVD_ERR_UNSUPPORTED: the rearranged row has no logical
  * token positions).  Workspace, chunking and outputs as kvd_decode_attn (use
  * pool_bf16 for kvd_decode_workspace_bytes).  KVD_ERR_DTYPE if pool_bf16 is

@@ -167,3 +167,28 @@ def test_one_precision_rows_equal_the_plain_kernels(env, mode):
                    lse_out=lse, chunk_tokens=chunk)
         torch.cuda.synchronize()
         assert torch.equal(out, out_m) and torch.equal(lse, lse_m), (mode, chunk)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rows_in_logical_order(env, d):
+    """A row may also list the blocks in their logical order, precisions
+    alternating (each entry names its own pool): the step over the same stored
+    tokens, for the library's chunking and for chunks that start mid-page."""
+    kvd, H, torch = env
+    from oracle import mixed
+    case = MixedCase(kvd, H, torch, d, seed=720 + d)
+    table = np.full((len(LENS), case.mb), -1, dtype=np.int32)
+    for i, s in enumerate(LENS):
+        for b in range(-(-s // 16)):
+            table[i, b] = case.phys[(i, b)] | (kvd.PRECISION_BIT if case.prec[i][b] else 0)
+    case.ctx = list(LENS)
+    qf = H.bf16_to_f64(case.q)
+    ref_o = np.zeros(qf.shape)
+    ref_l = np.zeros(qf.shape[:2])
+    for i in range(len(LENS)):
+        ref_o[i], ref_l[i] = mixed.decode_mixed(qf[i], [(k, v) for k, v, _ in case.stored_blocks(i)])
+    for chunk in (0, 16, 48, 96):
+        H.say(f"mixed logical order d={d} chunk={chunk}")
+        out, lse = case.run(kvd, torch, table, chunk)
+        H.assert_bf16_close(out, ref_o, what=f"mixed logical order d{d} chunk{chunk}")
+        H.assert_lse_close(lse, ref_l)
