@@ -230,7 +230,7 @@ kvd_status kvd_create_pool(const kvd_pool_desc* d, void* kv_base, float* scale_b
     return KVD_ERR_INVALID_ARG;
   }
   kvd_pool* p = new (std::nothrow) kvd_pool;
-  if (!p) return KVD_ERR_INVALID_ARG;
+  if (!p) return KVD_ERR_CAPACITY;                  // host memory
   PoolView& v = p->v;
   v.num_layers = d->num_layers;
   v.num_blocks = d->num_blocks;

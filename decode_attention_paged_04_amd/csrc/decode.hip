@@ -145,10 +145,10 @@ __device__ inline Unit locate_unit(const DecodeLaunch& a, int k) {
 }
 
 // KIND: kBf16 or kFp8 (one pool), or kMixed (a bf16 and an FP8 pool; each
-// table entry names its block's precision in kPrecisionBit -- the page header
-// -- and the two entries of a pair share it).  A mixed kernel runs its pairs
-// twice, a bf16 pass and an FP8 pass; in each pass a pair of the other
-// precision is skipped like a dropped block, so every pass keeps the
+// table entry names its block's precision in kPrecisionBit -- the page
+// header).  A mixed kernel runs two passes, bf16 then FP8, each over the span
+// of pairs that holds blocks of its precision; inside a pass an entry of the
+// other precision is skipped like a dropped block, so every pass keeps the
 // one-precision pipeline (fixed loads in flight, one register set) and the
 // softmax state carries from the first pass into the second.
 template <int D, int KIND, bool FINAL, bool SCORES>

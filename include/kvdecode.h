@@ -100,7 +100,8 @@ kvd_status kvd_pool_bytes(const kvd_pool_desc* desc, size_t* kv_bytes, size_t* s
 /* Create a host handle over caller-owned device memory laid out as above.
  * kv_base: device pointer to kv_bytes bytes, 16-byte aligned.
  * scale_base: device pointer to scale_bytes bytes (FP8), NULL for bf16.
- * Host only: makes no HIP call.  *out is set only on KVD_OK. */
+ * Host only: makes no HIP call.  *out is set only on KVD_OK;
+ * KVD_ERR_CAPACITY if the host handle cannot be allocated. */
 kvd_status kvd_create_pool(const kvd_pool_desc* desc, void* kv_base, float* scale_base,
                            kvd_pool** out);
 kvd_status kvd_destroy_pool(kvd_pool* pool);
