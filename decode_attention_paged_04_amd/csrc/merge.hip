@@ -22,10 +22,11 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-// One workgroup of four waves per (sequence, query head); wave w owns the
-// channels [w*D/4, (w+1)*D/4).  lse = M + ln(sum_c exp(lse_c - M)) with M =
-// max_c lse_c over all n_chunks chunks; out = sum_c exp(lse_c - lse) * o_c,
-// rounded to bf16.  The o_c of a chunk whose weight is 0 (lse_c = -inf) is
+// Splits of more than kFewChunks chunks (see merge_few_kernel below): one
+// workgroup of four waves per (sequence, query head); wave w owns the channels
+// [w*D/4, (w+1)*D/4).  lse = M + ln(sum_c exp(lse_c - M)) with M = max_c
+// lse_c over all n_chunks chunks; out = sum_c exp(lse_c - lse) * o_c, rounded
+// to bf16.  The o_c of a chunk whose weight is 0 (lse_c = -inf) is
 // loaded but never used, so it may hold anything, NaN included.  No chunk, or
 // only empty ones: out = 0, lse = -inf.
 // Every wave computes M and the sum itself with shuffles (no LDS, no
@@ -108,6 +109,65 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   }
 }
 
+// The same merge for splits of at most kFewChunks chunks, one wave per
+// (sequence, query head) and four heads per workgroup: with many heads and few
+// chunks (a large batch of short contexts) a workgroup per head would make
+// the launch mostly workgroup dispatch.  Lane l takes channels l, l + 64, ...
+// and all the chunks; lane c holds lse_c.  All partial outputs are loaded
+// before the reductions, and each channel's sum runs in chunk order.
+constexpr int kFewChunks = 16;
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_few_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, int64_t n_heads,
+    int32_t n_chunks, uint16_t* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ lse2) {
+  constexpr int PER = D / 64;                    // channels per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t ih = (int64_t)blockIdx.x * (kMergeThreads / 64) + (threadIdx.x >> 6);
+  if (ih >= n_heads) return;                     // the whole wave
+  const int nc = n_chunks;                       // 1 .. kFewChunks
+  const float* pl = part_lse + ih * nc;
+  const float* po = part_o + ih * nc * D + lane;
+  float ov[kFewChunks][PER];
+#pragma unroll
+  for (int c = 0; c < kFewChunks; ++c)
+#pragma unroll
+    for (int p = 0; p < PER; ++p) ov[c][p] = c < nc ? po[(size_t)c * D + 64 * p] : 0.f;
+  const float lv = lane < nc ? pl[lane] : -INFINITY;
+  const float M = wave_max(lv);
+  uint16_t* o = out + ih * D + lane;
+  if (M == -INFINITY) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) o[64 * p] = 0;
+    if (lane == 0) {
+      if (lse_out) lse_out[ih] = -INFINITY;
+      if (lse2) lse2[ih] = -INFINITY;
+    }
+    return;
+  }
+  const float lse = M + logf(wave_sum(lane < nc ? expf(lv - M) : 0.f));
+  const float wl = lane < nc ? expf(lv - lse) : 0.f;
+  float acc[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) acc[p] = 0.f;
+#pragma unroll
+  for (int c = 0; c < kFewChunks; ++c) {
+    if (c < nc) {                                // uniform
+      const float w = __shfl(wl, c);
+      if (w != 0.f) {                            // uniform: an empty chunk's o_c is never used
+#pragma unroll
+        for (int p = 0; p < PER; ++p) acc[p] += w * ov[c][p];
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PER; ++p) o[64 * p] = float_to_bf16_bits(acc[p]);
+  if (lane == 0) {
+    if (lse_out) lse_out[ih] = lse;
+    if (lse2) lse2[ih] = lse * kLog2eMerge;
+  }
+}
+
 // Slot of token t in the score scratch.  Within each 32-token pair the decode
 // kernel holds tokens 8G .. 8G+7 in lane group G and stores the first four of
 // every group, then the last four: token 8G + 4h + e goes to slot 16h + 4G + e.
@@ -156,6 +216,17 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ lo
 hipError_t launch_merge(const float* part_o, const float* part_lse, int32_t b, int32_t n_q,
                         int32_t n_chunks, int32_t head_dim, uint16_t* out, float* lse_out,
                         float* lse2, hipStream_t stream) {
+  if (n_chunks <= kFewChunks) {
+    const int64_t heads = (int64_t)b * n_q;
+    const dim3 grid((unsigned)((heads + kMergeThreads / 64 - 1) / (kMergeThreads / 64)));
+    if (head_dim == 128)
+      hipLaunchKernelGGL(merge_few_kernel<128>, grid, dim3(kMergeThreads), 0, stream, part_o, part_lse, heads,
+                         n_chunks, out, lse_out, lse2);
+    else
+      hipLaunchKernelGGL(merge_few_kernel<64>, grid, dim3(kMergeThreads), 0, stream, part_o, part_lse, heads,
+                         n_chunks, out, lse_out, lse2);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((size_t)b * n_q));
   if (head_dim == 128)
     hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, part_o, part_lse,

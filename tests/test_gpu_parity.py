@@ -219,22 +219,31 @@ def test_block_placement_and_reruns_are_bit_identical(env):
         assert torch.equal(l, outs[0][1])
 
 
-def test_merge_partials_export(env):
+@pytest.mark.parametrize("nc", [1, 2, 6, 16, 17, 40, 100])
+@pytest.mark.parametrize("d", [64, 128])
+def test_merge_partials_export(env, nc, d):
+    """Both merge kernels (up to 16 chunks: one wave per head, four heads per
+    workgroup -- 15 heads leave the last workgroup part empty; more chunks: a
+    workgroup per head), an empty chunk whose partial holds NaN, and a head
+    with every chunk empty."""
     kvd, H, W, torch = env
     from oracle import attention
-    rng = np.random.default_rng(5)
-    b, n_q, nc, d = 3, 4, 6, 128
+    rng = np.random.default_rng(5 + nc + d)
+    b, n_q = 3, 5
     part_o = rng.standard_normal((b, n_q, nc, d)).astype(np.float32)
     part_lse = (rng.standard_normal((b, n_q, nc)) * 3).astype(np.float32)
-    part_lse[0, 1, 2] = -np.inf
-    part_o[0, 1, 2] = 0
+    if nc > 1:
+        part_lse[0, 1, nc // 2] = -np.inf             # an empty chunk: its o_c is never read
+        part_o[0, 1, nc // 2] = np.nan
     part_lse[1, 2, :] = -np.inf                   # all chunks empty
-    ref_o, ref_lse = attention.merge_partials(part_o.astype(np.float64), part_lse.astype(np.float64))
+    part_o[1, 2, :] = np.nan
+    clean = np.where(np.isnan(part_o), 0.0, part_o)    # what an empty chunk means to the oracle
+    ref_o, ref_lse = attention.merge_partials(clean.astype(np.float64), part_lse.astype(np.float64))
     out = torch.empty((b, n_q, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((b, n_q), dtype=torch.float32, device="cuda")
     kvd.kvd_merge_partials(torch.from_numpy(part_o).cuda(), torch.from_numpy(part_lse).cuda(), out, lse)
     torch.cuda.synchronize()
-    H.assert_bf16_close(out, ref_o, what="merge")
+    H.assert_bf16_close(out, ref_o, what=f"merge nc={nc} d={d}")
     H.assert_lse_close(lse, ref_lse)
     assert torch.all(out[1, 2] == 0)
 
