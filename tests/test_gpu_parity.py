@@ -369,6 +369,30 @@ def test_fused_cumulative_scores(env, fp8, chunk):
         assert np.array_equal(got[i, s:], init[i, s:].astype(np.float64))
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("chunk", [0, 64, 160])
+def test_score_increments_alone(env, fp8, chunk):
+    """The score update with the array starting at zero, so that the 1e-5
+    relative bound applies to each token's increment itself (a nonzero start
+    would dominate it): three layers, every token of every sequence."""
+    kvd, H, W, torch = env
+    w = _workload(W, 4, 128, fp8=fp8, seed=610, layers=3)
+    lens = [1, 17, 64, 200, 513, 1000]
+    case = _case(H, W, w, lens=lens)
+    stride = case.max_ctx + 3
+    score = torch.zeros((len(lens), stride), dtype=torch.float32, device="cuda")
+    for layer in range(3):
+        case.run(layer, chunk=chunk, score=score, weight=1.0 / 3)
+    torch.cuda.synchronize()
+    got = score.cpu().double().numpy()
+    ref = case.oracle_scores(np.zeros((len(lens), stride)), range(len(lens)), 1.0 / 3)
+    for i, s in enumerate(lens):
+        assert np.all(ref[i, :s] > 0) and np.all(got[i, s:] == 0)
+    err = H.score_rel_error(got, ref)
+    H.say(f"score increments fp8={fp8} chunk={chunk}: max rel error {err:.2e}")
+    assert err <= H.TOL_SCORE_REL, err
+
+
 def test_tiny_workload(env):
     kvd, H, W, torch = env
     w = W.WORKLOADS["tiny"]
