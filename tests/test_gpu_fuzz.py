@@ -201,3 +201,65 @@ def test_random_mixed_precision(env, seed):
         ref_o[i], ref_l[i] = mixed.decode_mixed(qf[i], blocks)
     H.assert_bf16_close(out, ref_o, what=f"mixed fuzz seed {seed}")
     H.assert_lse_close(lse, ref_l)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_fused_append(env, seed):
+    """Random draws for kvd_decode_attn_append: the one launch that stores
+    token s_i - 1 and decodes must leave the pool, output and lse bit for bit
+    as kvd_write_kv followed by the plain decode does (some new rows scaled up
+    so that FP8 tiles re-quantise, some sequences' last block not attended)."""
+    kvd, H, W, torch = env
+    rng = np.random.default_rng(7000 + seed)
+    b = int(rng.integers(1, 16))
+    lens = rng.integers(0, 400, b)
+    lens[rng.random(b) < 0.15] = 0
+    lens[rng.random(b) < 0.15] = 16 * rng.integers(1, 20)       # the new token fills a block
+    n_kv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    fp8 = bool(rng.random() < 0.5)
+    chunk = int(rng.choice([0, 16, 48, 96, 512]))
+    H.say(f"fused append fuzz seed={seed}: b={b} n_kv={n_kv} g={g} d={d} fp8={fp8} chunk={chunk}")
+    w = W.DecodeWorkload(f"appendfz{seed}", seed=8000 + seed, b=b, layers=1, n_q=g * n_kv, n_kv=n_kv,
+                         head_dim=d, ctx=("fixed", 0), kv_dtype="fp8" if fp8 else "bf16")
+    lens = lens.astype(np.int32)
+    table, nb = W.block_tables(w, lens, pad_value=-1)
+    case = H.PagedCase(w, lens=lens, table=table, num_blocks=nb)
+    run_table = case.table.copy()
+    for i, s in enumerate(lens):
+        if s > 0 and rng.random() < 0.15:
+            run_table[i, (int(s) - 1) // 16] = -1                  # nothing stored, block not attended
+    tg = torch.Generator().manual_seed(9000 + seed)
+    new_k = torch.randn((b, n_kv, d), generator=tg)
+    new_v = torch.randn((b, n_kv, d), generator=tg)
+    grow = torch.from_numpy(np.where(rng.random(b) < 0.3, 30.0, 1.0).astype(np.float32))
+    new_k = (new_k * grow[:, None, None]).to(torch.bfloat16).cuda()
+    new_v = (new_v * grow.flip(0)[:, None, None]).to(torch.bfloat16).cuda()
+    slots = []
+    for i, s in enumerate(lens):
+        p = int(run_table[i, (int(s) - 1) // 16]) if s > 0 else -1
+        slots.append(p * 16 + (int(s) - 1) % 16 if s > 0 and p >= 0 else -1)
+    table_t = torch.from_numpy(run_table).cuda()
+    d_ = case.pool.desc
+    pools = []
+    for _ in range(2):
+        p = kvd.allocate_pool(d_.num_layers, d_.num_blocks, d_.n_kv, d_.head_dim, d_.dtype)
+        p.kv.copy_(case.pool.kv)
+        if fp8:
+            p.scales.copy_(case.pool.scales)
+        pools.append(p)
+    kvd.kvd_write_kv(pools[0], 0, new_k, new_v, torch.tensor(slots, dtype=torch.int32, device="cuda"))
+    res = []
+    for pool, fused in ((pools[0], False), (pools[1], True)):
+        out = torch.empty_like(case.q[0])
+        lse = torch.empty(case.q[0].shape[:2], dtype=torch.float32, device="cuda")
+        kvd.decode(pool, 0, case.q[0], table_t, case.lens_t, max(case.max_ctx, 1), out=out, lse_out=lse,
+                   chunk_tokens=chunk, new_k=new_k if fused else None, new_v=new_v if fused else None)
+        res.append((out, lse))
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][0].view(torch.int16), res[1][0].view(torch.int16))
+    assert torch.equal(res[0][1], res[1][1])
+    assert torch.equal(pools[0].kv, pools[1].kv)
+    if fp8:
+        assert torch.equal(pools[0].scales.view(torch.int32), pools[1].scales.view(torch.int32))
