@@ -259,7 +259,8 @@ kvd_status kvd_write_kv(const kvd_pool* pool, int32_t layer, const void* k, cons
   if (n_tok == 0) return KVD_OK;
   if (!k || !v || !slot_mapping) return KVD_ERR_INVALID_ARG;
   // the bf16 store runs one work-item per element: fewer than 2^32 per launch
-  if ((int64_t)n_tok * pool->v.n_kv * pool->v.head_dim >= ((int64_t)1 << 32)) return KVD_ERR_UNSUPPORTED;
+  if (pool->v.dtype == KVD_BF16 && (int64_t)n_tok * pool->v.n_kv * pool->v.head_dim >= ((int64_t)1 << 32))
+    return KVD_ERR_UNSUPPORTED;
   clear_stale_error();
   KVD_TRY_HIP(kvd::launch_write(pool->v, layer, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                         slot_mapping, n_tok, static_cast<hipStream_t>(hip_stream)));
