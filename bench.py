@@ -18,7 +18,11 @@ Reported:
 * roofline    -- the decode kernel alone: algorithmic bytes per launch over
                  its mean duration, from a HIP event pair around a run of
                  back-to-back launches of it;
-* cpu_baseline-- the float64 oracle timed on a bounded sample on the host.
+* cpu_baseline-- the float64 oracle timed on a bounded sample on the host;
+* hbm_context -- context for the roofline: a plain streaming read of the
+                 headline launch's bytes with the decode kernels' own loads
+                 (the practical ceiling of a launch that size), and torch's
+                 copy and sum rates over 1 GiB.
 
 Timing details: inputs are resident in HBM before the timed region; the step
 sequence is captured in HIP graphs (one launch per layer call) and replayed,
@@ -561,6 +565,58 @@ def append_entry(name: str, calls: int):
     return e
 
 
+def hbm_context(launch_bytes: int, nbytes: int = 1 << 30, reps: int = 20):
+    """The box's own read and copy rates, as context for the roofline (not a
+    bound the decode must meet):
+    * stream_read -- libkvdecode's plain streaming read (the decode kernels'
+      own 16-byte non-temporal loads and nothing else) of launch_bytes, the
+      headline decode launch's size, cycling through 8 buffers (more than the
+      256 MB Infinity Cache) at several grid sizes: the best is the practical
+      ceiling of a launch that size;
+    * copy, read_torch -- torch's device-to-device copy (read + write counted)
+      and torch's sum (read only) over nbytes of fp32.
+    Each is timed with HIP events over repeated calls after a warm-up."""
+    import torch
+    import decode_attention_paged_04_amd as kvd
+    st = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        for k in range(3):
+            fn(k)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for k in range(n):
+            fn(k)
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3          # us per call
+
+    sb = launch_bytes // 16 * 16
+    bufs = [torch.empty(sb, dtype=torch.uint8, device="cuda") for _ in range(8)]
+    by_grid = {}
+    for grid in (256, 512, 1024, 2048):
+        sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+        by_grid[grid] = timed(lambda k: kvd.kvd_debug_stream_read(bufs[k % 8], sink, grid), 200)
+    best = min(by_grid, key=by_grid.get)
+    del bufs
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+    copy_us = timed(lambda k: dst.copy_(src), reps)
+    read_us = timed(lambda k: torch.sum(src, dim=0, out=acc), reps)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"stream_read": {"bytes": sb, "buffers": 8, "grid": best, "us": round(by_grid[best], 2),
+                            "GBs": round(sb / by_grid[best] / 1e3, 1),
+                            "us_by_grid": {str(g): round(u, 2) for g, u in by_grid.items()},
+                            "kernel": "kvd_debug_stream_read (the decode kernels' loads only)"},
+            "copy": {"bytes": nbytes, "us": round(copy_us, 2),
+                     "GBs_read_plus_write": round(2 * nbytes / copy_us / 1e3, 1),
+                     "kernel": "torch copy_ (device to device)"},
+            "read_torch": {"bytes": nbytes, "us": round(read_us, 2), "GBs": round(nbytes / read_us / 1e3, 1),
+                           "kernel": "torch sum over fp32"}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -648,6 +704,13 @@ def main():
             appends.append(append_entry(name, 200))
 
     traffic = measured_traffic(args.workload)
+    try:
+        context = hbm_context(head["launch_bytes"])
+        context["decode_launch_vs_stream_read"] = round(context["stream_read"]["us"] / head["launch_us"], 4)
+        log(f"hbm context: {context}")
+    except Exception as e:                     # context only: never costs the line
+        log(f"hbm context not measured: {e}")
+        context = None
     line = {
         "metric": METRIC,
         "value": round(head["value"], 2),
@@ -669,6 +732,7 @@ def main():
                      "traffic": traffic, "launch_us": round(head["launch_us"], 3),
                      "bytes_per_launch": head["launch_bytes"]},
         "cpu_baseline": cpu,
+        "hbm_context": context,
         "secondary": secondary,
         "extra": extras,
         "tiered": tiered,

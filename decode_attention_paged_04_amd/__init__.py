@@ -70,6 +70,7 @@ EXPORTS = {
                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p),
     "kvd_debug_fp8_decode": (ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p),
+    "kvd_debug_stream_read": (ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p),
     # host block bookkeeping (kvblocks.h)
     "kvd_bm_create": (ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)),
     "kvd_bm_destroy": (ctypes.c_void_p,),
@@ -388,6 +389,18 @@ def kvd_debug_fp8_decode(codes, out, stream=None):
     _check_tensor(out, "out", (int(codes.numel()),), torch.float32, codes.device)
     _check(lib.kvd_debug_fp8_decode(_ptr(codes), int(codes.numel()), _ptr(out), _stream(stream)),
            "kvd_debug_fp8_decode")
+
+
+def kvd_debug_stream_read(data, sink, grid: int, stream=None):
+    """Stream-read every byte of ``data`` (a contiguous device tensor, a
+    multiple of 16 bytes) with the decode kernels' loads; ``sink``: uint32
+    ``[grid * 256]``, the per-work-item XOR of the words read."""
+    import torch
+    nbytes = int(data.numel()) * data.element_size()
+    _require(data.is_contiguous() and data.is_cuda, "data must be a contiguous device tensor")
+    _check_tensor(sink, "sink", (int(grid) * 256,), torch.int32, data.device)
+    _check(lib.kvd_debug_stream_read(_ptr(data), nbytes, _ptr(sink), int(grid), _stream(stream)),
+           "kvd_debug_stream_read")
 
 
 def decode(pool: Pool, layer: int, q, block_table, context_lens, max_context_len: int, out=None,

@@ -370,4 +370,14 @@ kvd_status kvd_debug_fp8_decode(const uint8_t* codes, int32_t n, float* out, voi
   return KVD_OK;
 }
 
+kvd_status kvd_debug_stream_read(const void* data, uint64_t bytes, uint32_t* sink, int32_t grid,
+                                 void* hip_stream) {
+  if (!data || !sink || grid < 1 || grid > 65536) return KVD_ERR_INVALID_ARG;
+  if (bytes < 16 || bytes % 16 != 0 || ((uintptr_t)data & 15) != 0) return KVD_ERR_INVALID_ARG;
+  if (bytes >= ((uint64_t)1 << 32)) return KVD_ERR_UNSUPPORTED;
+  clear_stale_error();
+  KVD_TRY_HIP(kvd::launch_stream_read(data, (uint32_t)bytes, sink, grid, static_cast<hipStream_t>(hip_stream)));
+  return KVD_OK;
+}
+
 }  // extern "C"

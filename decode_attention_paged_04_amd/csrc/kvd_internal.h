@@ -86,4 +86,7 @@ hipError_t launch_debug_offsets(const PoolView& p, int32_t layer, const int32_t*
 hipError_t launch_debug_fp8_decode(const uint8_t* codes, int32_t n, float* out,
                                    hipStream_t stream);
 
+hipError_t launch_stream_read(const void* data, uint32_t bytes, uint32_t* sink, int32_t grid,
+                              hipStream_t stream);
+
 }  // namespace kvd

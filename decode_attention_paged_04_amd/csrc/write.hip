@@ -1,5 +1,6 @@
 // Storing new tokens into the pool (bf16 copy, FP8 E4M3 quantisation) and the
-// test hooks that expose the decode kernels' addressing and FP8 widening.
+// test hooks that expose the decode kernels' addressing, FP8 widening and
+// streaming read.
 #include "device_common.h"
 #include "kv_store.h"
 #include "kvd_internal.h"
@@ -155,6 +156,36 @@ hipError_t launch_debug_fp8_decode(const uint8_t* codes, int32_t n, float* out,
   const int groups = (n + 7) / 8;
   hipLaunchKernelGGL(debug_fp8_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
                      stream, codes, n, out);
+  return hipGetLastError();
+}
+
+// A plain streaming read of `bytes` bytes with the decode kernels' 16-byte
+// non-temporal buffer loads: workgroup w reads 16-byte units w*256*U + u*256 +
+// thread, then steps by grid*256*U units, with U loads in flight per thread;
+// each thread XORs every 32-bit word it read into sink[w*256 + thread].
+template <int U>
+__global__ __launch_bounds__(256) void stream_read_kernel(const void* __restrict__ data, uint32_t bytes,
+                                                         uint32_t* __restrict__ sink) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(data, bytes);
+  const uint32_t units = bytes / 16;
+  const uint32_t stride = gridDim.x * 256u * U;
+  uint32_t acc = 0;
+  for (uint32_t base = blockIdx.x * 256u * U; base < units; base += stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t k = base + 256u * u + threadIdx.x;
+      v[u] = load16(r, k < units ? k * 16u : kOutOfRange);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  sink[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+hipError_t launch_stream_read(const void* data, uint32_t bytes, uint32_t* sink, int32_t grid,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(stream_read_kernel<8>, dim3((unsigned)grid), dim3(256), 0, stream, data, bytes, sink);
   return hipGetLastError();
 }
 

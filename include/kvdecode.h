@@ -296,6 +296,18 @@ kvd_status kvd_debug_gather_offsets(const kvd_pool* pool, int32_t layer, const i
  * codes: device uint8 [n]; out: device fp32 [n]. */
 kvd_status kvd_debug_fp8_decode(const uint8_t* codes, int32_t n, float* out, void* hip_stream);
 
+/* A plain streaming read of `bytes` bytes at `data` with the decode kernels'
+ * own 16-byte non-temporal loads and nothing else -- the read rate those loads
+ * reach on this device, the practical ceiling of a decode launch of the same
+ * size (Spherical KV summary §1: decode time is the time to stream the pages).
+ * data: device, 16-byte aligned; bytes: a multiple of 16, at least 16 and
+ * below 2^32 (else KVD_ERR_UNSUPPORTED); grid: 1 .. 65536 workgroups of 256
+ * work-items; sink: device uint32 [grid * 256], each entry the XOR of the
+ * 32-bit words its work-item read (so the XOR of all entries is the XOR of
+ * every word of the buffer). */
+kvd_status kvd_debug_stream_read(const void* data, uint64_t bytes, uint32_t* sink, int32_t grid,
+                                 void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -264,3 +264,15 @@ def test_launch_size_limits():
     assert _status("kvd_decode_attn", pool.handle, 0, ctypes.byref(heads), None) == 2
     assert _status("kvd_write_kv", pool.handle, 0, FAKE, FAKE, FAKE, 1 << 24, None) == 2   # 2^32 elements
     assert _status("kvd_merge_partials", FAKE, FAKE, 1 << 21, 8, 4, 128, FAKE, None, None) == 2
+
+
+def test_stream_read_argument_errors():
+    f = "kvd_debug_stream_read"
+    assert _status(f, None, 1 << 20, FAKE, 512, None) == 1            # no data
+    assert _status(f, FAKE, 1 << 20, None, 512, None) == 1            # no sink
+    assert _status(f, FAKE, 1000, FAKE, 512, None) == 1               # not a multiple of 16
+    assert _status(f, FAKE, 0, FAKE, 512, None) == 1                  # empty
+    assert _status(f, FAKE + 8, 1 << 20, FAKE, 512, None) == 1        # misaligned
+    assert _status(f, FAKE, 1 << 20, FAKE, 0, None) == 1              # no workgroups
+    assert _status(f, FAKE, 1 << 20, FAKE, 65537, None) == 1          # too many
+    assert _status(f, FAKE, 1 << 32, FAKE, 512, None) == 2            # beyond one buffer resource
