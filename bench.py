@@ -565,14 +565,15 @@ def append_entry(name: str, calls: int):
     return e
 
 
-def hbm_context(launch_bytes: int, nbytes: int = 1 << 30, reps: int = 20):
+def hbm_context(launch_bytes: int, secondary_bytes: int = 0, nbytes: int = 1 << 30, reps: int = 20):
     """The box's own read and copy rates, as context for the roofline (not a
     bound the decode must meet):
     * stream_read -- libkvdecode's plain streaming read (the decode kernels'
       own 16-byte non-temporal loads and nothing else) of launch_bytes, the
       headline decode launch's size, cycling through 8 buffers (more than the
       256 MB Infinity Cache) at several grid sizes: the best is the practical
-      ceiling of a launch that size;
+      ceiling of a launch that size; stream_read_secondary likewise for the
+      secondary workload's launch (one buffer, already beyond the cache);
     * copy, read_torch -- torch's device-to-device copy (read + write counted)
       and torch's sum (read only) over nbytes of fp32.
     Each is timed with HIP events over repeated calls after a warm-up."""
@@ -591,14 +592,24 @@ def hbm_context(launch_bytes: int, nbytes: int = 1 << 30, reps: int = 20):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n * 1e3          # us per call
 
-    sb = launch_bytes // 16 * 16
-    bufs = [torch.empty(sb, dtype=torch.uint8, device="cuda") for _ in range(8)]
-    by_grid = {}
-    for grid in (256, 512, 1024, 2048):
-        sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
-        by_grid[grid] = timed(lambda k: kvd.kvd_debug_stream_read(bufs[k % 8], sink, grid), 200)
-    best = min(by_grid, key=by_grid.get)
-    del bufs
+    def stream_read(nb: int, nbuf: int, n: int):
+        sb = nb // 16 * 16
+        bufs = [torch.empty(sb, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+        by_grid = {}
+        for grid in (256, 512, 1024, 2048):
+            sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+            by_grid[grid] = timed(lambda k: kvd.kvd_debug_stream_read(bufs[k % nbuf], sink, grid), n)
+        best = min(by_grid, key=by_grid.get)
+        del bufs
+        torch.cuda.empty_cache()
+        return {"bytes": sb, "buffers": nbuf, "grid": best, "us": round(by_grid[best], 2),
+                "GBs": round(sb / by_grid[best] / 1e3, 1),
+                "us_by_grid": {str(g): round(u, 2) for g, u in by_grid.items()},
+                "kernel": "kvd_debug_stream_read (the decode kernels' loads only)"}
+
+    out = {"stream_read": stream_read(launch_bytes, 8, 200)}
+    if secondary_bytes and secondary_bytes < (1 << 32):
+        out["stream_read_secondary"] = stream_read(secondary_bytes, 1, 20)
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     acc = torch.empty((), dtype=torch.float32, device="cuda")
@@ -606,15 +617,11 @@ def hbm_context(launch_bytes: int, nbytes: int = 1 << 30, reps: int = 20):
     read_us = timed(lambda k: torch.sum(src, dim=0, out=acc), reps)
     del src, dst
     torch.cuda.empty_cache()
-    return {"stream_read": {"bytes": sb, "buffers": 8, "grid": best, "us": round(by_grid[best], 2),
-                            "GBs": round(sb / by_grid[best] / 1e3, 1),
-                            "us_by_grid": {str(g): round(u, 2) for g, u in by_grid.items()},
-                            "kernel": "kvd_debug_stream_read (the decode kernels' loads only)"},
-            "copy": {"bytes": nbytes, "us": round(copy_us, 2),
-                     "GBs_read_plus_write": round(2 * nbytes / copy_us / 1e3, 1),
-                     "kernel": "torch copy_ (device to device)"},
-            "read_torch": {"bytes": nbytes, "us": round(read_us, 2), "GBs": round(nbytes / read_us / 1e3, 1),
-                           "kernel": "torch sum over fp32"}}
+    out["copy"] = {"bytes": nbytes, "us": round(copy_us, 2), "GBs_read_plus_write": round(2 * nbytes / copy_us / 1e3, 1),
+                   "kernel": "torch copy_ (device to device)"}
+    out["read_torch"] = {"bytes": nbytes, "us": round(read_us, 2), "GBs": round(nbytes / read_us / 1e3, 1),
+                         "kernel": "torch sum over fp32"}
+    return out
 
 
 def main():
@@ -705,8 +712,11 @@ def main():
 
     traffic = measured_traffic(args.workload)
     try:
-        context = hbm_context(head["launch_bytes"])
+        context = hbm_context(head["launch_bytes"], sec["launch_bytes"] if secondary else 0)
         context["decode_launch_vs_stream_read"] = round(context["stream_read"]["us"] / head["launch_us"], 4)
+        if "stream_read_secondary" in context:
+            context["secondary_launch_vs_stream_read"] = round(
+                context["stream_read_secondary"]["us"] / sec["launch_us"], 4)
         log(f"hbm context: {context}")
     except Exception as e:                     # context only: never costs the line
         log(f"hbm context not measured: {e}")
