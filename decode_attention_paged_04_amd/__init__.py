@@ -189,6 +189,8 @@ def kvd_write_kv(pool: Pool, layer: int, k, v, slot_mapping, stream=None):
     _check_tensor(slot_mapping, "slot_mapping", (n,), torch.int32)
     _check_tensor(k, "k", shape, torch.bfloat16, slot_mapping.device)
     _check_tensor(v, "v", shape, torch.bfloat16, slot_mapping.device)
+    _require_gpu(slot_mapping, "slot_mapping")
+    _require(pool.kv.device == slot_mapping.device, "the pool and the new rows must share a device")
     _check(lib.kvd_write_kv(pool.handle, layer, _ptr(k), _ptr(v), _ptr(slot_mapping), n, _stream(stream)),
            "kvd_write_kv")
 
@@ -216,6 +218,11 @@ def slot_mapping_for(block_table, context_lens):
 def _require(cond: bool, msg: str):
     if not cond:
         raise ValueError(msg)
+
+
+def _require_gpu(t, name: str):
+    """The library takes device pointers only: a host tensor never reaches it."""
+    _require(t.is_cuda, f"{name} must be on a GPU (the library reads device memory only)")
 
 
 def _check_tensor(t, name: str, shape, dtype, device=None):
@@ -316,6 +323,7 @@ def kvd_decode_attn_mixed(pool_bf16: Pool, pool_fp8: Pool, layer: int, args: Dec
     (table entries of FP8 blocks carry bit 30; see kvd_mixed_row)."""
     _require(pool_fp8.desc.n_kv == pool_bf16.desc.n_kv and pool_fp8.desc.head_dim == pool_bf16.desc.head_dim,
              "the two pools differ in shape")
+    _require(pool_fp8.kv.device == pool_bf16.kv.device, "the two pools must share a device")
     _check(lib.kvd_decode_attn_mixed(pool_bf16.handle, pool_fp8.handle, layer, ctypes.byref(args),
                                      _stream(stream)), "kvd_decode_attn_mixed")
 
@@ -363,6 +371,7 @@ def kvd_merge_partials(part_o, part_lse, out, lse_out=None, stream=None):
     _check_tensor(part_o, "part_o", (b, n_q, nc, d), torch.float32)
     _check_tensor(part_lse, "part_lse", (b, n_q, nc), torch.float32, part_o.device)
     _check_tensor(out, "out", (b, n_q, d), torch.bfloat16, part_o.device)
+    _require_gpu(part_o, "part_o")
     if lse_out is not None:
         _check_tensor(lse_out, "lse_out", (b, n_q), torch.float32, part_o.device)
     _check(lib.kvd_merge_partials(_ptr(part_o), _ptr(part_lse), b, n_q, nc, d, _ptr(out), _ptr(lse_out),
@@ -379,6 +388,7 @@ def kvd_debug_gather_offsets(pool: Pool, layer: int, block_table, n_tok: int, ou
     _check_tensor(block_table, "block_table", (b, mb), torch.int32)
     _check_tensor(out_k, "out_k", (b, pool.desc.n_kv, n_tok), torch.int64, block_table.device)
     _check_tensor(out_v, "out_v", (b, pool.desc.n_kv, n_tok), torch.int64, block_table.device)
+    _require_gpu(block_table, "block_table")
     _check(lib.kvd_debug_gather_offsets(pool.handle, layer, _ptr(block_table), mb, b, n_tok, _ptr(out_k),
                                         _ptr(out_v), _stream(stream)), "kvd_debug_gather_offsets")
 
@@ -387,6 +397,7 @@ def kvd_debug_fp8_decode(codes, out, stream=None):
     import torch
     _check_tensor(codes, "codes", (int(codes.numel()),), torch.uint8)
     _check_tensor(out, "out", (int(codes.numel()),), torch.float32, codes.device)
+    _require_gpu(codes, "codes")
     _check(lib.kvd_debug_fp8_decode(_ptr(codes), int(codes.numel()), _ptr(out), _stream(stream)),
            "kvd_debug_fp8_decode")
 
@@ -397,7 +408,8 @@ def kvd_debug_stream_read(data, sink, grid: int, stream=None):
     ``[grid * 256]``, the per-work-item XOR of the words read."""
     import torch
     nbytes = int(data.numel()) * data.element_size()
-    _require(data.is_contiguous() and data.is_cuda, "data must be a contiguous device tensor")
+    _require(data.is_contiguous(), "data must be contiguous")
+    _require_gpu(data, "data")
     _check_tensor(sink, "sink", (int(grid) * 256,), torch.int32, data.device)
     _check(lib.kvd_debug_stream_read(_ptr(data), nbytes, _ptr(sink), int(grid), _stream(stream)),
            "kvd_debug_stream_read")

@@ -276,3 +276,26 @@ def test_stream_read_argument_errors():
     assert _status(f, FAKE, 1 << 20, FAKE, 0, None) == 1              # no workgroups
     assert _status(f, FAKE, 1 << 20, FAKE, 65537, None) == 1          # too many
     assert _status(f, FAKE, 1 << 32, FAKE, 512, None) == 2            # beyond one buffer resource
+
+
+def test_binding_refuses_host_tensors():
+    """Every wrapper of a device-side call refuses host tensors before the
+    library sees a pointer (a host address read by a kernel would fault)."""
+    import torch
+    pool = _pool()                                   # host handle over a stand-in address
+    pool_t = kvd.Pool(pool.desc, torch.zeros(16, dtype=torch.uint8), None, None)
+    k = torch.zeros((4, pool.desc.n_kv, pool.desc.head_dim), dtype=torch.bfloat16)
+    slots = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        kvd.kvd_write_kv(pool_t, 0, k, k.clone(), slots)
+    part_o = torch.zeros((1, 2, 3, 128))
+    with pytest.raises(ValueError, match="GPU"):
+        kvd.kvd_merge_partials(part_o, torch.zeros((1, 2, 3)), torch.zeros((1, 2, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="GPU"):
+        kvd.kvd_debug_fp8_decode(torch.zeros(8, dtype=torch.uint8), torch.zeros(8))
+    with pytest.raises(ValueError, match="GPU"):
+        kvd.kvd_debug_gather_offsets(pool_t, 0, torch.zeros((1, 2), dtype=torch.int32), 32,
+                                     torch.zeros((1, pool.desc.n_kv, 32), dtype=torch.int64),
+                                     torch.zeros((1, pool.desc.n_kv, 32), dtype=torch.int64))
+    with pytest.raises(ValueError, match="GPU"):
+        kvd.kvd_debug_stream_read(torch.zeros(64, dtype=torch.uint8), torch.zeros(256, dtype=torch.int32), 1)
