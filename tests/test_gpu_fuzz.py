@@ -42,7 +42,9 @@ def _draw(seed):
     return rng, lens.astype(np.int32), n_kv, g, d, fp8, chunk, drop
 
 
-@pytest.mark.parametrize("seed", range(CASES))
+# seed 1049: a small output (one live sequence, d_h 64) where one element's exact
+# value sits 1.4e-4 bf16 spacings from a rounding midpoint -- a rounding tie
+@pytest.mark.parametrize("seed", list(range(CASES)) + [1049])
 def test_random_configuration(env, seed):
     kvd, H, W, torch = env
     from oracle import tiers
@@ -52,7 +54,7 @@ def test_random_configuration(env, seed):
     w = W.DecodeWorkload(f"fuzz{seed}", seed=2000 + seed, b=len(lens), layers=1, n_q=g * n_kv, n_kv=n_kv,
                          head_dim=d, ctx=("fixed", 0), kv_dtype="fp8" if fp8 else "bf16")
     table, nb = W.block_tables(w, lens, pad_value=-1)
-    case = H.PagedCase(w, lens=lens, table=table, num_blocks=nb)
+    case = H.PagedCase(w, lens=lens, table=table, num_blocks=max(nb, 1))   # all-empty batches too
     run_table = case.table.copy()
     if drop:
         for i, s in enumerate(lens):
@@ -92,7 +94,7 @@ def test_random_configuration_with_scores(env, seed):
     w = W.DecodeWorkload(f"fuzzs{seed}", seed=4000 + seed, b=len(lens), layers=1, n_q=g * n_kv, n_kv=n_kv,
                          head_dim=d, ctx=("fixed", 0), kv_dtype="fp8" if fp8 else "bf16")
     table, nb = W.block_tables(w, lens, pad_value=-1)
-    case = H.PagedCase(w, lens=lens, table=table, num_blocks=nb)
+    case = H.PagedCase(w, lens=lens, table=table, num_blocks=max(nb, 1))   # all-empty batches too
     run_table = case.table.copy()
     if drop:
         for i, s in enumerate(lens):
@@ -225,7 +227,7 @@ def test_random_fused_append(env, seed):
                          head_dim=d, ctx=("fixed", 0), kv_dtype="fp8" if fp8 else "bf16")
     lens = lens.astype(np.int32)
     table, nb = W.block_tables(w, lens, pad_value=-1)
-    case = H.PagedCase(w, lens=lens, table=table, num_blocks=nb)
+    case = H.PagedCase(w, lens=lens, table=table, num_blocks=max(nb, 1))   # all-empty batches too
     run_table = case.table.copy()
     for i, s in enumerate(lens):
         if s > 0 and rng.random() < 0.15:
