@@ -9,10 +9,20 @@ needs HBM").  Output and lse must match the oracle's step over the attended
 tokens, to the tolerances of the other parity tests; a second set of draws
 adds the fused cumulative score and checks its update as well.
 """
+import os
+
 import numpy as np
 import pytest
 
 pytestmark = pytest.mark.gpu
+
+# KVD_FUZZ_SEEDS=n runs n seeds of every kind instead (a long sweep).
+_SWEEP = int(os.environ.get("KVD_FUZZ_SEEDS", "0"))
+
+
+def _seeds(n: int):
+    return range(_SWEEP) if _SWEEP > 0 else range(n)
+
 
 CASES = 24
 
@@ -44,7 +54,7 @@ def _draw(seed):
 
 # seed 1049: a small output (one live sequence, d_h 64) where one element's exact
 # value sits 1.4e-4 bf16 spacings from a rounding midpoint -- a rounding tie
-@pytest.mark.parametrize("seed", list(range(CASES)) + [1049])
+@pytest.mark.parametrize("seed", sorted(set(_seeds(CASES)) | {1049}))
 def test_random_configuration(env, seed):
     kvd, H, W, torch = env
     from oracle import tiers
@@ -80,7 +90,7 @@ def test_random_configuration(env, seed):
     H.assert_lse_close(lse, ref_l)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", _seeds(16))
 def test_random_configuration_with_scores(env, seed):
     """The same kind of draw with a fused cumulative score (chunks of whole
     32-token pairs): output and the score update against the oracle."""
@@ -126,7 +136,7 @@ def test_random_configuration_with_scores(env, seed):
     assert err <= H.TOL_SCORE_REL, err
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", _seeds(12))
 def test_random_mixed_precision(env, seed):
     """Random draws for kvd_decode_attn_mixed: each block of each sequence
     in the bf16 or the FP8 pool at random, rows built by kvd_mixed_row, random
@@ -205,7 +215,7 @@ def test_random_mixed_precision(env, seed):
     H.assert_lse_close(lse, ref_l)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", _seeds(12))
 def test_random_fused_append(env, seed):
     """Random draws for kvd_decode_attn_append: the one launch that stores
     token s_i - 1 and decodes must leave the pool, output and lse bit for bit
