@@ -275,3 +275,113 @@ def test_random_fused_append(env, seed):
     assert torch.equal(pools[0].kv, pools[1].kv)
     if fp8:
         assert torch.equal(pools[0].scales.view(torch.int32), pools[1].scales.view(torch.int32))
+
+
+@pytest.mark.parametrize("seed", _seeds(12))
+def test_random_append_schedule(env, seed):
+    """Random prompt and final lengths, random tokens per append call, some
+    rows scaled up so that FP8 tiles change scale mid-block: after every call
+    the FP8 codes and scales equal the oracle's append step bit for bit (bf16:
+    the stored rows equal the inputs), and the decode over the result matches
+    the oracle."""
+    kvd, H, W, torch = env
+    from oracle import attention, e4m3, paged
+    rng = np.random.default_rng(11000 + seed)
+    b = int(rng.integers(1, 9))
+    final = rng.integers(1, 120, b)
+    prefix = np.minimum(final, rng.integers(0, 60, b))
+    n_kv = int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    fp8 = bool(rng.random() < 0.7)
+    H.say(f"append schedule seed={seed}: b={b} final={final.tolist()} prefix={prefix.tolist()} n_kv={n_kv} "
+          f"d={d} fp8={fp8}")
+    w = W.DecodeWorkload(f"appsch{seed}", seed=12000 + seed, b=b, layers=1, n_q=2 * n_kv, n_kv=n_kv,
+                         head_dim=d, ctx=("fixed", 0), kv_dtype="fp8" if fp8 else "bf16")
+    lens = final.astype(np.int32)
+    table, nb = W.block_tables(w, lens)
+    offs = W.offsets(lens)
+    n = int(offs[-1])
+    K, V = W.keys_values(w, 0, n, "cpu")
+    Kf, Vf = H.bf16_to_f64(K).astype(np.float32), H.bf16_to_f64(V).astype(np.float32)
+    big = rng.random(n) < 0.03                     # a few large rows: scales grow mid-block
+    Kf[big] *= 30.0
+    Vf[big[::-1]] *= 20.0
+    K = torch.from_numpy(Kf).to(torch.bfloat16)
+    V = torch.from_numpy(Vf).to(torch.bfloat16)
+    Kf, Vf = H.bf16_to_f64(K).astype(np.float32), H.bf16_to_f64(V).astype(np.float32)
+    Kd, Vd = K.cuda(), V.cuda()
+    pool = kvd.allocate_pool(1, nb, n_kv, d, kvd.KVD_FP8_E4M3 if fp8 else kvd.KVD_BF16)
+    pool.kv.fill_(0xFF)
+    state = {i: [np.zeros((0, n_kv, d), np.uint8), np.zeros((0, n_kv), np.float32),
+                 np.zeros((0, n_kv, d), np.uint8), np.zeros((0, n_kv), np.float32)] for i in range(b)}
+    lay = paged.PoolLayout(1, nb, n_kv, d, elem_bytes=1 if fp8 else 2)
+    done = [0] * b
+    first = True
+    while any(dn < f for dn, f in zip(done, final)):
+        idx, slots, ranges = [], [], []
+        for i in range(b):
+            if done[i] >= final[i]:
+                continue
+            step = int(prefix[i]) if first else int(rng.choice([0, 1, 1, 1, 2, 5, 17]))
+            e = min(int(final[i]), done[i] + step)
+            if e > done[i]:
+                ranges.append((i, done[i], e))
+                idx += [int(offs[i]) + t for t in range(done[i], e)]
+                slots += [int(table[i, t // 16]) * 16 + t % 16 for t in range(done[i], e)]
+                done[i] = e
+        first = False
+        if not idx:
+            continue
+        it = torch.tensor(idx, dtype=torch.long)
+        kvd.kvd_write_kv(pool, 0, Kd[it.cuda()].contiguous(), Vd[it.cuda()].contiguous(),
+                         torch.tensor(slots, dtype=torch.int32, device="cuda"))
+        if fp8:
+            for i, lo, hi in ranges:
+                a = int(offs[i])
+                ck, sk, cv, sv = state[i]
+                ck, sk = e4m3.append_sequence(ck, sk, Kf[a + lo:a + hi])
+                cv, sv = e4m3.append_sequence(cv, sv, Vf[a + lo:a + hi])
+                state[i] = [ck, sk, cv, sv]
+        torch.cuda.synchronize()
+        got = pool.kv.cpu().numpy()
+        got_sc = pool.scales.cpu().numpy() if fp8 else None
+        for i, lo, hi in ranges:
+            k_idx, v_idx = paged.gather_indices(lay, 0, table[i], hi)
+            if fp8:
+                ck, sk, cv, sv = state[i]
+                assert np.array_equal(got[k_idx], ck) and np.array_equal(got[v_idx], cv), (i, lo, hi)
+                for blk in range(sk.shape[0]):
+                    p = int(table[i, blk])
+                    for j in range(n_kv):
+                        assert got_sc[lay.scale_index(0, p, j, 0)].view(np.uint32) == sk[blk, j].view(np.uint32)
+                        assert got_sc[lay.scale_index(0, p, j, 1)].view(np.uint32) == sv[blk, j].view(np.uint32)
+            else:
+                a = int(offs[i])
+                kb = got.view(np.uint16)
+                assert np.array_equal(kb[k_idx], H_bits(K[a:a + hi])), (i, lo, hi)
+                assert np.array_equal(kb[v_idx], H_bits(V[a:a + hi])), (i, lo, hi)
+    q = W.query(w, 0, "cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    kvd.decode(pool, 0, q, torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda(), int(lens.max()),
+               out=out, lse_out=lse)
+    torch.cuda.synchronize()
+    qf = H.bf16_to_f64(q)
+    ref_o = np.zeros(qf.shape)
+    ref_l = np.zeros(qf.shape[:2])
+    for i, s in enumerate(final):
+        a = int(offs[i])
+        if fp8:
+            ck, sk, cv, sv = state[i]
+            Kl, Vl = e4m3.dequantize_sequence(ck, sk), e4m3.dequantize_sequence(cv, sv)
+        else:
+            Kl, Vl = Kf[a:a + s].astype(np.float64), Vf[a:a + s].astype(np.float64)
+        ref_o[i], ref_l[i] = attention.decode_sequence(qf[i], Kl, Vl)
+    H.assert_bf16_close(out, ref_o, what=f"append schedule seed {seed}")
+    H.assert_lse_close(lse, ref_l)
+
+
+def H_bits(t):
+    """bf16 tensor -> its raw uint16 bits (logical [s][n_kv][d] order)."""
+    import torch
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
