@@ -67,9 +67,10 @@ __device__ inline int qk_channel0(int c, int G) { return 32 * c + 8 * G; }
 // Launch order of the (sequence, chunk) units.  Per KV head the grid holds
 // b * n_chunks units, n_chunks covering the longest allowed context, but a
 // sequence of s tokens fills only ceil(s / chunk) of its chunks.  Workgroup x
-// takes KV head x % n_kv and unit k = x / n_kv of this order, in three runs,
-// each sequence by sequence: the full chunks, then the partly filled last
-// chunks, then the empty chunks.  The hardware hands out workgroups in grid
+// takes KV head x % n_kv and unit k = x / n_kv of this order, in three runs:
+// the full chunks (chunk-major when 1 < b <= 64 and n_chunks <= 64, else
+// sequence by sequence), then the partly filled last chunks, then the empty
+// chunks, sequence by sequence.  The hardware hands out workgroups in grid
 // order, so the shorter units run last and the final workgroups drain sooner;
 // an empty chunk only marks itself empty for the merge (or writes a zero
 // output), and at the end of the grid such workgroups no longer hold compute
@@ -122,7 +123,26 @@ __device__ inline Unit locate_unit(const DecodeLaunch& a, int k) {
     const int full = sl / a.chunk;
     return run == 0 ? 0 : (run == 1 ? full : full + (sl % a.chunk != 0 ? 1 : 0));
   };
-  if (per == 1) {                                      // lane li owns just sequence li
+  if (per == 1) {                                      // lane l owns just sequence l
+    if (run == 0 && a.b > 1 && a.n_chunks <= 64) {
+      // Full chunks chunk-major: chunk c of every sequence that has it, in
+      // sequence order, then chunk c + 1.  Sequences that share prefix blocks
+      // then read them together, from one XCD's L2 (the workgroups of one KV
+      // head share an XCD).  The order only decides which workgroup computes
+      // a unit, never its arithmetic.
+      int kr = kk, c = 0;
+      for (;;) {                                       // uniform; ends since kk < n_full
+        const uint64_t m = __ballot(nf > c);
+        const int cnt_c = __popcll(m);
+        if (kr < cnt_c) {
+          const int rank = __popcll(m & ((1ull << lane) - 1ull));
+          const int i = __builtin_ctzll(__ballot(((m >> lane) & 1ull) && rank == kr));
+          return Unit{i, c, __shfl(s1, i)};
+        }
+        kr -= cnt_c;
+        ++c;
+      }
+    }
     const int sl = __shfl(s1, li);
     return Unit{li, first_of(sl) + kq, sl};
   }
