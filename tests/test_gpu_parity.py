@@ -402,3 +402,27 @@ def test_tiny_workload(env):
     ref_o, ref_lse = case.oracle(0)
     H.assert_bf16_close(out, ref_o, what="tiny")
     H.assert_lse_close(lse, ref_lse)
+
+
+@pytest.mark.parametrize("b", [2, 64])
+def test_chunk_major_order_edges(env, b):
+    """The chunk-major order of full chunks (1 < b <= 64, n_chunks <= 64) at its
+    edges: up to 64 sequences (lane 63 owns one), exactly 64 chunks of 16
+    tokens, sequences with no full chunk, with every chunk full, and empty
+    ones.  Every unit must be computed once: outputs and lse against the
+    oracle."""
+    kvd, H, W, torch = env
+    rng = np.random.default_rng(50 + b)
+    lens = rng.integers(0, 1025, b).astype(np.int32)
+    lens[0] = 1024                                     # all 64 chunks full
+    lens[-1] = 1024 if b > 2 else 7                    # the last lane
+    if b > 4:
+        lens[1], lens[2], lens[3] = 0, 15, 16          # empty, no full chunk, one full chunk
+    w = _workload(W, 4, 64, seed=51 + b)
+    w = w.with_(b=b)
+    case = _case(H, W, w, lens=lens)
+    out, lse = case.run(0, chunk=16)
+    torch.cuda.synchronize()
+    ref_o, ref_l = case.oracle(0)
+    H.assert_bf16_close(out, ref_o, what=f"chunk-major b={b}")
+    H.assert_lse_close(lse, ref_l)
