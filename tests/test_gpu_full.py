@@ -104,3 +104,41 @@ def test_full_8b_fp8_with_scores(env):
         err = H.score_rel_error(got[i], ref[i])
         H.say(f"scores seq {i}: max rel error {err:.2e}")
         assert err <= H.TOL_SCORE_REL
+
+
+def test_full_shared_prefix_batch(env):
+    """The shared-prefix workload the benchmark times (32 requests behind one
+    16,384-token prompt stored once, 1,024 own tokens each; one layer, the
+    library's chunking, whose full chunks run chunk-major): sampled sequences
+    against the oracle over each one's logical K/V -- the prompt's rows as
+    stored by request 0, then its own."""
+    kvd, H, W, torch = env
+    from oracle import attention
+    w = W.WORKLOADS["8b_prefix"].with_(layers=1)
+    lens = W.context_lengths(w)
+    table, nb = W.block_tables(w, lens)
+    offs = W.offsets(lens)
+    n = int(offs[-1])
+    table_t, lens_t = torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda()
+    slots = kvd.slot_mapping_for(table_t, lens_t)
+    for i in range(1, w.b):                          # the prompt is stored once, by request 0
+        slots[int(offs[i]):int(offs[i]) + w.shared_prefix] = -1
+    pool = kvd.allocate_pool(1, nb, w.n_kv, w.head_dim, kvd.KVD_BF16)
+    K, V = W.keys_values(w, 0, n, "cuda")
+    kvd.kvd_write_kv(pool, 0, K, V, slots)
+    q = W.query(w, 0, "cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    kvd.decode(pool, 0, q, table_t, lens_t, int(lens.max()), out=out, lse_out=lse)
+    torch.cuda.synchronize()
+    qf = H.bf16_to_f64(q)
+    Kc, Vc = K.cpu(), V.cpu()
+    P = w.shared_prefix
+    for i in (0, 13, 31):
+        a, e = int(offs[i]), int(offs[i + 1])
+        Ki = torch.cat([Kc[:P], Kc[a + P:e]]) if i else Kc[a:e]
+        Vi = torch.cat([Vc[:P], Vc[a + P:e]]) if i else Vc[a:e]
+        ref_o, ref_l = attention.decode_sequence(qf[i], H.bf16_to_f64(Ki), H.bf16_to_f64(Vi))
+        mx, rel = H.assert_bf16_close(out[i], ref_o, what=f"shared prefix seq {i}")
+        H.say(f"shared prefix seq {i}: max-abs {mx:.2e} rel-L2 {rel:.2e}")
+        H.assert_lse_close(lse[i:i + 1], ref_l[None])
