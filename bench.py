@@ -635,7 +635,7 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="chunk_tokens (0 = the library's choice)")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas (0 = enough to exceed the cache)")
     ap.add_argument("--launches", type=int, default=200, help="event-timed launches for the roofline")
-    ap.add_argument("--extras", default="8b_ragged,8b_fp8_scores,70b_shard,8b_prefix,8b_batch256",
+    ap.add_argument("--extras", default="8b_ragged,8b_fp8_scores,70b_shard,8b_prefix,8b_prefix256,8b_batch256",
                     help="further workloads reported in the same line (comma list), or 'none'")
     ap.add_argument("--no-append", action="store_true", help="skip the append-cost entries")
     ap.add_argument("--no-tiered", action="store_true", help="skip the tier-restricted entry")

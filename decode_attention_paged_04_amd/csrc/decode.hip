@@ -68,7 +68,7 @@ __device__ inline int qk_channel0(int c, int G) { return 32 * c + 8 * G; }
 // b * n_chunks units, n_chunks covering the longest allowed context, but a
 // sequence of s tokens fills only ceil(s / chunk) of its chunks.  Workgroup x
 // takes KV head x % n_kv and unit k = x / n_kv of this order, in three runs:
-// the full chunks (chunk-major when 1 < b <= 64 and n_chunks <= 64, else
+// the full chunks (chunk-major when 1 < b <= 512 and n_chunks <= 64, else
 // sequence by sequence), then the partly filled last chunks, then the empty
 // chunks, sequence by sequence.  The hardware hands out workgroups in grid
 // order, so the shorter units run last and the final workgroups drain sooner;
@@ -102,12 +102,27 @@ __device__ inline Unit locate_unit(const DecodeLaunch& a, int k) {
   };
   const int per = (a.b + 63) >> 6;              // sequences per lane
   int nf = 0, np = 0, s1 = 0;                   // this lane's full and partly filled chunks
+  int nfs[8];                                   // per <= 8: full chunks of each of its sequences
+  if (per <= 8) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      nfs[m] = 0;
+      if (m < per) {
+        const int sl = length(lane * per + m);
+        nfs[m] = sl / a.chunk;
+        nf += nfs[m];
+        np += sl % a.chunk != 0 ? 1 : 0;
+        s1 = sl;
+      }
+    }
+  } else {
 #pragma unroll 8
-  for (int m = 0; m < per; ++m) {
-    const int sl = length(lane * per + m);
-    nf += sl / a.chunk;
-    np += sl % a.chunk != 0 ? 1 : 0;
-    s1 = sl;
+    for (int m = 0; m < per; ++m) {
+      const int sl = length(lane * per + m);
+      nf += sl / a.chunk;
+      np += sl % a.chunk != 0 ? 1 : 0;
+      s1 = sl;
+    }
   }
   const int owned = max(0, min(a.b, (lane + 1) * per) - lane * per);
   const int nd = owned * a.n_chunks - nf - np;  // its empty chunks
@@ -145,6 +160,44 @@ __device__ inline Unit locate_unit(const DecodeLaunch& a, int k) {
     }
     const int sl = __shfl(s1, li);
     return Unit{li, first_of(sl) + kq, sl};
+  }
+  if (run == 0 && per <= 8 && a.n_chunks <= 64) {
+    // The same chunk-major order over several sequences per lane.  F(c), the
+    // number of full chunks with index below c, is found by a wave sum; a
+    // binary search gives the chunk index c with F(c) <= kk < F(c + 1), then
+    // a prefix sum over the lanes and a walk over the owning lane's sequences
+    // give the (kk - F(c))-th sequence that has chunk c.
+    auto F = [&](int c) {
+      int t = 0;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) t += min(nfs[m], c);
+      return __builtin_amdgcn_readfirstlane(__shfl(wave_inclusive_sum(t), 63));
+    };
+    int lo_c = 0, hi_c = a.n_chunks;                   // F(lo_c) <= kk < F(hi_c) = n_full
+    while (hi_c - lo_c > 1) {
+      const int mid = (lo_c + hi_c) >> 1;
+      if (F(mid) <= kk) lo_c = mid;
+      else hi_c = mid;
+    }
+    const int c = lo_c;
+    const int kr = kk - F(c);
+    int cl = 0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) cl += nfs[m] > c ? 1 : 0;
+    const int inc = wave_inclusive_sum(cl);
+    const int l2 = __popcll(__ballot(inc <= kr));
+    int r = __builtin_amdgcn_readfirstlane(kr - __shfl(inc - cl, l2));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int v = __builtin_amdgcn_readfirstlane(__shfl(nfs[m], l2));
+      if (m < per && v > c) {
+        if (r == 0) {
+          const int q = l2 * per + m;
+          return Unit{q, c, length(q)};
+        }
+        --r;
+      }
+    }
   }
   for (int m0 = 0; m0 < per; m0 += 64) {
     const int q = li * per + m0 + lane;

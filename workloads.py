@@ -74,6 +74,10 @@ WORKLOADS = {
     "8b_prefix": DecodeWorkload("llama3.1-8b-8layer-b32-shared16k+1k", seed=7, b=32, layers=8,
                                 n_q=32, n_kv=8, head_dim=128, ctx=("fixed", 17408),
                                 shared_prefix=16384),
+    # a serving batch of 256 requests behind one 8,192-token system prompt
+    "8b_prefix256": DecodeWorkload("llama3.1-8b-8layer-b256-shared8k+512", seed=9, b=256, layers=8,
+                                   n_q=32, n_kv=8, head_dim=128, ctx=("fixed", 8704),
+                                   shared_prefix=8192),
     # a large serving batch: 256 requests of 1k..4k tokens
     "8b_batch256": DecodeWorkload("llama3.1-8b-32layer-b256-s1k..4k", seed=8, b=256, layers=32,
                                   n_q=32, n_kv=8, head_dim=128, ctx=("uniform", 1024, 4096)),
