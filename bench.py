@@ -594,6 +594,8 @@ def hbm_context(launch_bytes: int, secondary_bytes: int = 0, nbytes: int = 1 << 
 
     def stream_read(nb: int, nbuf: int, n: int):
         sb = nb // 16 * 16
+        if sb >= (1 << 32):                      # beyond one buffer resource: not measured
+            return None
         bufs = [torch.empty(sb, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
         by_grid = {}
         for grid in (256, 512, 1024, 2048):
@@ -713,8 +715,9 @@ def main():
     traffic = measured_traffic(args.workload)
     try:
         context = hbm_context(head["launch_bytes"], sec["launch_bytes"] if secondary else 0)
-        context["decode_launch_vs_stream_read"] = round(context["stream_read"]["us"] / head["launch_us"], 4)
-        if "stream_read_secondary" in context:
+        if context["stream_read"]:
+            context["decode_launch_vs_stream_read"] = round(context["stream_read"]["us"] / head["launch_us"], 4)
+        if context.get("stream_read_secondary"):
             context["secondary_launch_vs_stream_read"] = round(
                 context["stream_read_secondary"]["us"] / sec["launch_us"], 4)
         log(f"hbm context: {context}")
