@@ -102,7 +102,7 @@ class Workload:
         dev = "cuda"
         self.lens_t = torch.from_numpy(self.lens).to(dev)
         self.table_t = torch.from_numpy(self.table).to(dev)
-        slots = kvd.slot_mapping_for(self.table_t, self.lens_t)
+        slots = kvd.kvd_slot_mapping(self.table_t, self.lens_t)
         n_tok = int(self.lens.sum())
         offs = W.offsets(self.lens)
         for i in range(1, w.b):                 # a shared prefix is stored once, by sequence 0
@@ -255,8 +255,7 @@ class Workload:
         call alone and the decode call with the append fused, both replayed
         from graphs)."""
         torch, kvd, w = self.torch, self.kvd, self.w
-        last = torch.from_numpy(self.table[np.arange(w.b), (self.lens - 1) // 16] * 16 + (self.lens - 1) % 16)
-        slots = last.to(torch.int32).cuda()
+        slots = kvd.kvd_slot_mapping(self.table_t, self.lens_t, first_token=self.lens_t - 1)
         g = torch.Generator(device="cuda")
         g.manual_seed(w.seed)
         K = torch.randn((w.b, w.n_kv, w.head_dim), generator=g, device="cuda").to(torch.bfloat16)
@@ -486,14 +485,18 @@ def mixed_entry(name: str, layers: int, steps: int, fp8_share: float = 0.5):
             row.append(int(phys[bool(f8)][nxt[bool(f8)]]))
             nxt[bool(f8)] += 1
         ids.append(row)
-    offs = W.offsets(lens)
     n_tok = int(lens.sum())
-    slot = {False: np.full(n_tok, -1, np.int32), True: np.full(n_tok, -1, np.int32)}
-    for i, s in enumerate(lens):
-        for t in range(int(s)):
-            f8 = bool(prec[i][t // 16])
-            slot[f8][int(offs[i]) + t] = ids[i][t // 16] * 16 + t % 16
-    slot_t = {k: torch.from_numpy(v).cuda() for k, v in slot.items()}
+    # per pool, the logical block table of its own blocks (-1 elsewhere: slot -1, not stored)
+    nbmax = max(len(p) for p in prec)
+    lens_t = torch.from_numpy(lens).cuda()
+    slot_t = {}
+    for f8 in (False, True):
+        tab = np.full((w.b, nbmax), -1, np.int32)
+        for i, p in enumerate(prec):
+            for b in range(len(p)):
+                if bool(p[b]) == f8:
+                    tab[i, b] = ids[i][b]
+        slot_t[f8] = kvd.kvd_slot_mapping(torch.from_numpy(tab).cuda(), lens_t)
     qs = []
     for layer in range(layers):
         K, V = W.keys_values(w, layer, n_tok, "cuda")

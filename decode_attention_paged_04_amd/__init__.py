@@ -51,6 +51,8 @@ EXPORTS = {
     "kvd_destroy_pool": (ctypes.c_void_p,),
     "kvd_write_kv": (ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                      ctypes.c_int32, ctypes.c_void_p),
+    "kvd_slot_mapping": (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p),
     "kvd_decode_plan": (ctypes.c_void_p, ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_int32),
                         ctypes.POINTER(ctypes.c_int32)),
     "kvd_decode_workspace_bytes": (ctypes.c_void_p, ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)),
@@ -69,6 +71,7 @@ EXPORTS = {
     "kvd_debug_gather_offsets": (ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p),
+    "kvd_debug_unit_map": (ctypes.c_void_p, ctypes.POINTER(DecodeArgs), ctypes.c_void_p, ctypes.c_void_p),
     "kvd_debug_fp8_decode": (ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p),
     "kvd_debug_stream_read": (ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p),
     # host block bookkeeping (kvblocks.h)
@@ -195,24 +198,35 @@ def kvd_write_kv(pool: Pool, layer: int, k, v, slot_mapping, stream=None):
            "kvd_write_kv")
 
 
-def slot_mapping_for(block_table, context_lens):
-    """Caller-side helper: slots of every token of every sequence, packed in order.
-
-    Token t of sequence i goes to ``block_table[i][t // 16] * 16 + t % 16``
-    (the write call's slot convention).  Works on CPU or device tensors.
-    """
+def kvd_slot_mapping(block_table, context_lens, first_token=None, stream=None):
+    """Slot mapping of kvd_write_kv for tokens ``first_token[i] .. context_lens[i] - 1``
+    of every sequence (all tokens when ``first_token`` is None), packed in
+    sequence order; computed on the device by the library.  ``block_table``
+    int32 ``[b][max_blocks]``, ``context_lens`` and ``first_token`` int32 ``[b]``,
+    all on one GPU.  Returns int32 ``[n]`` on that device."""
     import torch
-    bt = block_table.to(torch.int64)
-    lens = context_lens.to(torch.int64).cpu().tolist()
-    _require(len(lens) == bt.shape[0], "one context length per block-table row")
-    _require(all(0 <= s <= BLOCK_SIZE * bt.shape[1] for s in lens), "context longer than its block-table row")
-    parts = []
-    for i, s in enumerate(lens):
-        t = torch.arange(s, device=bt.device)
-        parts.append(bt[i, t // BLOCK_SIZE] * BLOCK_SIZE + t % BLOCK_SIZE)
-    if not parts:
-        return torch.zeros(0, dtype=torch.int32, device=bt.device)
-    return torch.cat(parts).to(torch.int32)
+    _require(block_table is not None and block_table.dim() == 2, "block_table must be [b][max_blocks]")
+    b, mb = (int(x) for x in block_table.shape)
+    dev = block_table.device
+    _check_tensor(block_table, "block_table", (b, mb), torch.int32)
+    _require_gpu(block_table, "block_table")
+    _check_tensor(context_lens, "context_lens", (b,), torch.int32, dev)
+    if first_token is not None:
+        _check_tensor(first_token, "first_token", (b,), torch.int32, dev)
+    lens = context_lens.to(torch.int64)
+    first = first_token.to(torch.int64) if first_token is not None else torch.zeros_like(lens)
+    lh, fh = lens.cpu(), first.cpu()
+    _require(bool(((lh >= 0) & (lh <= BLOCK_SIZE * mb)).all()), "context longer than its block-table row")
+    _require(bool(((fh >= 0) & (fh <= lh)).all()), "first_token must lie in [0, context_lens]")
+    counts = lens - first
+    start = torch.cumsum(counts, 0) - counts if b else counts
+    n = int((lh - fh).sum())
+    slots = torch.empty(n, dtype=torch.int32, device=dev)
+    max_tok = int((lh - fh).max()) if b else 0
+    _check(lib.kvd_slot_mapping(_ptr(block_table), mb, b, _ptr(context_lens),
+                                _ptr(first_token), _ptr(start), max_tok, _ptr(slots), n, _stream(stream)),
+           "kvd_slot_mapping")
+    return slots
 
 
 def _require(cond: bool, msg: str):
@@ -391,6 +405,17 @@ def kvd_debug_gather_offsets(pool: Pool, layer: int, block_table, n_tok: int, ou
     _require_gpu(block_table, "block_table")
     _check(lib.kvd_debug_gather_offsets(pool.handle, layer, _ptr(block_table), mb, b, n_tok, _ptr(out_k),
                                         _ptr(out_v), _stream(stream)), "kvd_debug_gather_offsets")
+
+
+def kvd_debug_unit_map(pool: Pool, args: DecodeArgs, device="cuda", stream=None):
+    """(sequence, chunk, clamped length) of every workgroup of a decode launch
+    with ``args`` (workgroup x serves KV head x % n_kv), int32 ``[grid][3]``."""
+    import torch
+    _, nc = kvd_decode_plan(pool, args)
+    units = torch.full((int(args.b) * pool.desc.n_kv * nc, 3), -7, dtype=torch.int32, device=device)
+    _check(lib.kvd_debug_unit_map(pool.handle, ctypes.byref(args), _ptr(units), _stream(stream)),
+           "kvd_debug_unit_map")
+    return units
 
 
 def kvd_debug_fp8_decode(codes, out, stream=None):

@@ -267,6 +267,21 @@ kvd_status kvd_write_kv(const kvd_pool* pool, int32_t layer, const void* k, cons
   return KVD_OK;
 }
 
+kvd_status kvd_slot_mapping(const int32_t* block_table, int32_t max_blocks_per_seq, int32_t b,
+                            const int32_t* context_lens, const int32_t* first_token, const int64_t* out_start,
+                            int32_t max_tokens_per_seq, int32_t* slots, int64_t n_slots, void* hip_stream) {
+  if (b < 0 || max_blocks_per_seq < 1 || max_tokens_per_seq < 0 || n_slots < 0) return KVD_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks_per_seq * kvd::kBlock >= ((int64_t)1 << 31)) return KVD_ERR_UNSUPPORTED;
+  // 256-work-item workgroups: fewer than 2^32 work-items per launch
+  if ((int64_t)b * ((max_tokens_per_seq + 255) / 256) >= ((int64_t)1 << 24)) return KVD_ERR_UNSUPPORTED;
+  if (b == 0 || max_tokens_per_seq == 0 || n_slots == 0) return KVD_OK;
+  if (!block_table || !context_lens || !out_start || !slots) return KVD_ERR_INVALID_ARG;
+  clear_stale_error();
+  KVD_TRY_HIP(kvd::launch_slot_mapping(block_table, max_blocks_per_seq, b, context_lens, first_token, out_start,
+                                       max_tokens_per_seq, slots, n_slots, static_cast<hipStream_t>(hip_stream)));
+  return KVD_OK;
+}
+
 kvd_status kvd_decode_plan(const kvd_pool* pool, const kvd_decode_args* args, int32_t* chunk_tokens,
                            int32_t* n_chunks) {
   if (!pool) return KVD_ERR_INVALID_ARG;
@@ -358,6 +373,30 @@ kvd_status kvd_debug_gather_offsets(const kvd_pool* pool, int32_t layer, const i
   clear_stale_error();
   KVD_TRY_HIP(kvd::launch_debug_offsets(pool->v, layer, block_table, max_blocks_per_seq, b, n_tok, out_k, out_v,
                                 static_cast<hipStream_t>(hip_stream)));
+  return KVD_OK;
+}
+
+kvd_status kvd_debug_unit_map(const kvd_pool* pool, const kvd_decode_args* args, int32_t* units,
+                              void* hip_stream) {
+  if (!pool || !args) return KVD_ERR_INVALID_ARG;
+  DecodePlan pl;
+  kvd_status st = plan_decode(pool->v, args, &pl);
+  if (st != KVD_OK) return st;
+  if (args->b == 0) return KVD_OK;
+  if (!args->context_lens || !units) return KVD_ERR_INVALID_ARG;
+  kvd::DecodeLaunch L{};
+  L.context_lens = args->context_lens;
+  L.b = args->b;
+  L.n_q = args->n_q;
+  L.n_kv = pool->v.n_kv;
+  L.g = args->n_q / pool->v.n_kv;
+  L.max_blocks = args->max_blocks_per_seq;
+  L.num_blocks = pool->v.num_blocks;
+  L.ctx_bound = pl.ctx_bound;
+  L.chunk = pl.chunk;
+  L.n_chunks = pl.n_chunks;
+  clear_stale_error();
+  KVD_TRY_HIP(kvd::launch_debug_units(L, units, static_cast<hipStream_t>(hip_stream)));
   return KVD_OK;
 }
 

@@ -258,11 +258,13 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
   // token's K and V rows of head j into the pool, exactly as the write kernel
   // would, and then reads them back like every other row.  FP8: waves 0 and 1
   // re-quantise the K and the V tile; the new scales are kept in registers for
-  // this block, because the scalar cache may hold the old ones.
+  // this block, because the scalar cache may hold the old ones.  A context
+  // length above the bound has no slot for its new token inside the bound (s
+  // is the clamped length): nothing is stored, so no cached row is overwritten.
   int32_t app_pid = -1;
   float app_sK = 0.f, app_sV = 0.f;
   if constexpr (!MIX) {
-    if (a.new_k != nullptr && s > 0 && (s - 1) / a.chunk == c) {
+    if (a.new_k != nullptr && s > 0 && (s - 1) / a.chunk == c && load_invariant(a.context_lens + i) == s) {
       const int tl = s - 1;
       const int32_t pid = load_invariant(a.block_table + (size_t)i * a.max_blocks + tl / kBlock);
       if (pid >= 0 && pid < a.num_blocks) {
@@ -619,6 +621,26 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
       a.part_lse[ih * a.n_chunks + c] = lse2 * kLn2;
     }
   }
+}
+
+// Test hook: the unit each workgroup of a decode launch with these arguments
+// takes -- out[3x .. 3x+2] = (sequence, chunk, clamped context length) of
+// workgroup x, whose KV head is x % n_kv.  One wave per workgroup runs
+// locate_unit exactly as the decode kernels do.
+__global__ __launch_bounds__(64) void debug_units_kernel(DecodeLaunch a, int32_t* __restrict__ out) {
+  const int x = blockIdx.x;
+  const Unit u = locate_unit(a, x / a.n_kv);
+  if (threadIdx.x == 0) {
+    out[3 * (size_t)x] = u.i;
+    out[3 * (size_t)x + 1] = u.c;
+    out[3 * (size_t)x + 2] = u.s;
+  }
+}
+
+hipError_t launch_debug_units(const DecodeLaunch& a, int32_t* out, hipStream_t stream) {
+  const dim3 grid((unsigned)((size_t)a.n_chunks * a.b * a.n_kv));
+  hipLaunchKernelGGL(debug_units_kernel, grid, dim3(64), 0, stream, a, out);
+  return hipGetLastError();
 }
 
 template <int D, int KIND>

@@ -68,6 +68,8 @@ struct DecodeLaunch {
 hipError_t launch_decode(const DecodeLaunch& a, int head_dim, int kind, bool final_direct,
                          bool scores, hipStream_t stream);
 
+hipError_t launch_debug_units(const DecodeLaunch& a, int32_t* out, hipStream_t stream);
+
 hipError_t launch_merge(const float* part_o, const float* part_lse, int32_t b, int32_t n_q,
                         int32_t n_chunks, int32_t head_dim, uint16_t* out, float* lse_out,
                         float* lse2, hipStream_t stream);
@@ -78,6 +80,11 @@ hipError_t launch_score(const float* logits, const float* lse2, const int32_t* c
 
 hipError_t launch_write(const PoolView& p, int32_t layer, const uint16_t* k, const uint16_t* v,
                         const int32_t* slot_mapping, int32_t n_tok, hipStream_t stream);
+
+hipError_t launch_slot_mapping(const int32_t* block_table, int32_t max_blocks, int32_t b,
+                               const int32_t* context_lens, const int32_t* first_token,
+                               const int64_t* out_start, int32_t max_tokens, int32_t* slots,
+                               int64_t n_slots, hipStream_t stream);
 
 hipError_t launch_debug_offsets(const PoolView& p, int32_t layer, const int32_t* block_table,
                                 int32_t max_blocks, int32_t b, int32_t n_tok, int64_t* out_k,

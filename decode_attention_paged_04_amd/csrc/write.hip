@@ -99,6 +99,42 @@ hipError_t launch_write(const PoolView& pv, int32_t layer, const uint16_t* k, co
   return hipGetLastError();
 }
 
+// Slots of tokens [first_i, s_i) of every sequence i: token t lives in
+// physical block block_table[i][t / 16] at in-block row t % 16, slot
+// block * 16 + row.  Workgroup x serves sequence x / groups and its tokens
+// first_i + 256 (x % groups) + thread; the slot of token t goes to
+// slots[out_start[i] + t - first_i].
+__global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* __restrict__ bt, int32_t max_blocks,
+                                                           const int32_t* __restrict__ lens,
+                                                           const int32_t* __restrict__ first,
+                                                           const int64_t* __restrict__ out_start,
+                                                           int32_t groups, int32_t* __restrict__ slots,
+                                                           int64_t n_slots) {
+  const int i = blockIdx.x / groups;
+  const int cap = max_blocks * kBlock;
+  int s = lens[i];
+  s = s < 0 ? 0 : (s > cap ? cap : s);
+  int f = first ? first[i] : 0;
+  f = f < 0 ? 0 : (f > s ? s : f);
+  const int t = f + (int)(blockIdx.x % groups) * 256 + (int)threadIdx.x;
+  if (t >= s) return;
+  const int64_t o = out_start[i] + (t - f);
+  if (o < 0 || o >= n_slots) return;
+  const int32_t e = bt[(size_t)i * max_blocks + t / kBlock];
+  // a slot is an int32: blocks from 2^27 on have none
+  slots[o] = (e < 0 || e >= (1 << 27)) ? -1 : e * kBlock + t % kBlock;
+}
+
+hipError_t launch_slot_mapping(const int32_t* bt, int32_t max_blocks, int32_t b, const int32_t* lens,
+                               const int32_t* first, const int64_t* out_start, int32_t max_tokens,
+                               int32_t* slots, int64_t n_slots, hipStream_t stream) {
+  const int32_t groups = (max_tokens + 255) / 256;
+  if (groups == 0 || b == 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3((unsigned)((int64_t)b * groups)), dim3(256), 0, stream, bt,
+                     max_blocks, lens, first, out_start, groups, slots, n_slots);
+  return hipGetLastError();
+}
+
 // Element offsets of K[t][0] and V[t][0] through the decode kernels' rule.
 __global__ __launch_bounds__(256) void debug_offsets_kernel(int64_t layer_elem0, int32_t num_blocks,
                                                             int32_t n_kv, int32_t head_dim,

@@ -94,10 +94,16 @@ typedef struct kvd_pool kvd_pool;
 
 /* Bytes the caller must allocate for a pool: kv_bytes for K/V (256-byte
  * alignment recommended) and scale_bytes for FP8 scales (0 for bf16).
+ * kv_bytes is num_blocks * 16 tokens times the per-token size of froggydisk's
+ * section "토큰 하나의 크기": 2 (K and V) x layers x KV heads x head_dim x
+ * bytes per element (128 KiB for the Llama 3.1 8B shape in bf16, 320 KiB for
+ * 70B, half of that in FP8 -- section "KV 캐시를 줄이는 기법", FP8 paragraph).
  * Either output pointer may be NULL. */
 kvd_status kvd_pool_bytes(const kvd_pool_desc* desc, size_t* kv_bytes, size_t* scale_bytes);
 
-/* Create a host handle over caller-owned device memory laid out as above.
+/* Create a host handle over caller-owned device memory laid out as above:
+ * the memory cut up front into 16-token blocks that block tables then hand
+ * out (froggydisk, PagedAttention paragraph of section "KV 캐시를 줄이는 기법").
  * kv_base: device pointer to kv_bytes bytes, 16-byte aligned.
  * scale_base: device pointer to scale_bytes bytes (FP8), NULL for bf16.
  * Host only: makes no HIP call.  *out is set only on KVD_OK;
@@ -134,6 +140,34 @@ kvd_status kvd_destroy_pool(kvd_pool* pool);
  * element), else KVD_ERR_UNSUPPORTED. */
 kvd_status kvd_write_kv(const kvd_pool* pool, int32_t layer, const void* k, const void* v,
                         const int32_t* slot_mapping, int32_t n_tok, void* hip_stream);
+
+/* Slot mapping of kvd_write_kv from block tables: the paging rule of
+ * froggydisk's PagedAttention paragraph (section "KV 캐시를 줄이는 기법"):
+ * the block table says which physical block holds each 16-token logical
+ * block of a request, so token t of sequence i lives in physical block
+ * block_table[i][t / 16], in-block row t % 16, i.e. slot
+ * block_table[i][t / 16] * 16 + t % 16.
+ * block_table:  device int32 [b][max_blocks_per_seq].
+ * context_lens: device int32 [b]; s_i, clamped into [0, 16 * max_blocks_per_seq].
+ * first_token:  device int32 [b] or NULL (all 0); first_i, clamped into
+ *               [0, s_i].  Sequence i contributes its tokens first_i .. s_i - 1
+ *               (all of them for a prompt; the last one for a decode step).
+ * out_start:    device int64 [b]; token t of sequence i is written to
+ *               slots[out_start[i] + t - first_i] (packing is the caller's:
+ *               usually the exclusive prefix sum of s_i - first_i).
+ * max_tokens_per_seq: a host bound on every s_i - first_i (sizes the launch;
+ *               tokens beyond it are not written).
+ * slots:        device int32 [n_slots]; positions outside [0, n_slots) are
+ *               skipped.  A negative table entry (a block not present) or one
+ *               of 2^27 and above (no int32 slot) gives slot -1, which
+ *               kvd_write_kv skips.
+ * Errors: KVD_ERR_INVALID_ARG for negative sizes or a NULL pointer (other than
+ * first_token) when there is work; KVD_ERR_UNSUPPORTED when 16 *
+ * max_blocks_per_seq reaches 2^31 or b * ceil(max_tokens_per_seq / 256)
+ * reaches 2^24 (one launch of 256-work-item workgroups). */
+kvd_status kvd_slot_mapping(const int32_t* block_table, int32_t max_blocks_per_seq, int32_t b,
+                            const int32_t* context_lens, const int32_t* first_token, const int64_t* out_start,
+                            int32_t max_tokens_per_seq, int32_t* slots, int64_t n_slots, void* hip_stream);
 
 /* Arguments of one decode-attention call on one layer. */
 typedef struct {
@@ -219,7 +253,10 @@ kvd_status kvd_decode_attn_fp8(const kvd_pool* pool, int32_t layer, const kvd_de
  * that token: outputs, lse, score and pool contents equal those of
  * kvd_write_kv followed by the decode call, bit for bit.  The store is done by
  * the workgroups whose chunk holds token s_i - 1, before they read that block.
- * Nothing is stored for a sequence with s_i = 0 or whose last table entry is
+ * Nothing is stored for a sequence with s_i = 0, with a context length above
+ * min(max_context_len, 16 * max_blocks_per_seq) (its token has no slot inside
+ * that bound; the step then attends to the clamped context, as kvd_decode_attn
+ * does, and every cached row keeps its value), or whose last table entry is
  * negative or >= num_blocks.  Args, workspace and errors as kvd_decode_attn;
  * KVD_ERR_INVALID_ARG if new_k or new_v is NULL. */
 kvd_status kvd_decode_attn_append(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
@@ -262,6 +299,13 @@ kvd_status kvd_decode_partials(const kvd_pool* pool, int32_t layer, const kvd_de
                                float* part_o, float* part_lse, void* hip_stream);
 
 /* Merge per-chunk partial results by log-sum-exp.
+ * The attention step of froggydisk's section "KV 캐시란" (scores divided by
+ * sqrt(128), a softmax over them, the V rows summed with those weights) is a
+ * sum over the context's tokens; split into chunks, each chunk's normalised
+ * output o_c and log-sum-exp lse_c determine the whole exactly, which is what
+ * lets a long context be split over workgroups or over devices (the
+ * capacity-bound sharding of "The KV Cache Is the New Memory Wall" review,
+ * Tab. 5) and put together here.
  * part_o:   device fp32 [b][n_q][n_chunks][d_h], each chunk's normalised output
  * part_lse: device fp32 [b][n_q][n_chunks], natural log; -inf marks an empty
  *           chunk, which contributes nothing (its part_o row is never read)
@@ -291,6 +335,17 @@ const char* kvd_last_hip_error(void);
 kvd_status kvd_debug_gather_offsets(const kvd_pool* pool, int32_t layer, const int32_t* block_table,
                                     int32_t max_blocks_per_seq, int32_t b, int32_t n_tok,
                                     int64_t* out_k, int64_t* out_v, void* hip_stream);
+
+/* The work decomposition of a decode call with these arguments, as its
+ * kernels compute it: the grid holds b * n_kv * n_chunks workgroups
+ * (kvd_decode_plan), workgroup x serves KV head x % n_kv and one (sequence,
+ * chunk) unit, found on the device from the context lengths.  units: device
+ * int32 [b * n_kv * n_chunks][3], row x = (sequence, chunk, context length
+ * after clamping) of workgroup x.  Only args->b, n_q, max_blocks_per_seq,
+ * max_context_len, context_lens, chunk_tokens and score (which constrains the
+ * chunking) are used. */
+kvd_status kvd_debug_unit_map(const kvd_pool* pool, const kvd_decode_args* args, int32_t* units,
+                              void* hip_stream);
 
 /* Decode n E4M3 codes with the decode kernels' own widening routine.
  * codes: device uint8 [n]; out: device fp32 [n]. */

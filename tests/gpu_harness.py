@@ -15,20 +15,23 @@ from oracle import attention, e4m3, numerics, paged, scores
 
 DEV = "cuda"
 
-# Tolerances.  bf16 outputs are compared with the oracle rounded to bf16
-# (nearest even): relative L2 1e-3 per output tensor of one layer call, and per
-# element an absolute error of at most 4e-3 -- or of one bf16 spacing at the
-# reference value, which is what a single rounding-boundary flip costs when the
-# output's magnitude is 1 or more (the spacing there is 2^-7 or wider, so no
-# bf16 result could meet 4e-3 on its own).  FP8 pools: relative L2 1e-2
-# against the oracle run on the same E4M3 codes.  Cumulative scores: 1e-5
-# relative per element.
-# Rounding ties: an exact value that lies within the fp32 arithmetic's error of
-# a bf16 rounding midpoint has two correct bf16 results.  A kernel value equal
-# to the rounding of the reference moved by at most TIE_REL * |ref| + TIE_ABS *
-# max|ref| is counted as exact in the relative L2 (the per-element bound still
-# applies to it).  In a small output tensor a single such flip of a large
-# element would otherwise weigh more than 1e-3 on its own.
+# Tolerances.  Per element, the bf16 output is compared with the exact
+# (float64, unrounded) oracle: |got - ref| <= max(4e-3, half a bf16 spacing at
+# |ref| + the fp32 arithmetic's error).  Half a spacing is what rounding a
+# correct fp32 result to bf16 may cost; where |ref| >= 1 it exceeds 4e-3 on its
+# own, so no bf16 result could meet 4e-3 there.  Per output tensor of one
+# layer call: relative L2 1e-3 against the oracle rounded to bf16 (nearest
+# even) -- rounding exact values to bf16 alone gives a relative L2 of about
+# 1.7e-3, so the 1e-3 bound can only hold against the rounded oracle.  FP8
+# pools: relative L2 1e-2 against the oracle run on the same E4M3 codes (same
+# per-element bound).  Cumulative scores: 1e-5 relative per element.
+# The fp32 arithmetic's error is taken as TIE_REL * |ref| + TIE_ABS *
+# max|ref| (2^-16 relative plus 2^-20 of the tensor's largest magnitude).
+# Rounding ties: an exact value that lies within that error of a bf16
+# rounding midpoint has two correct bf16 results.  A kernel value equal to the
+# rounding of the reference moved by at most that error counts as exact in the
+# relative L2.  In a small output tensor a single such flip of a large element
+# would otherwise weigh more than 1e-3 on its own.
 TIE_REL = 2.0 ** -16
 TIE_ABS = 2.0 ** -20
 TOL_MAX_ABS = 4e-3
@@ -47,21 +50,22 @@ def bf16_to_f64(t) -> np.ndarray:
 
 
 def bf16_errors(got, ref_f64: np.ndarray):
-    """(max-abs, rel-L2, worst element error over its allowance) of bf16 ``got``
-    against the oracle rounded to bf16 (rounding ties, see TIE_REL, count as
-    exact in the rel-L2)."""
+    """(max-abs against the exact oracle, rel-L2 against the oracle rounded to
+    bf16, worst element error over its allowance) of bf16 ``got`` (rounding
+    ties, see TIE_REL, count as exact in the rel-L2)."""
     g = bf16_to_f64(got)
     ref = np.asarray(ref_f64, dtype=np.float64)
     r = numerics.round_to_bf16(ref)
-    err = np.abs(g - r)
-    t = TIE_REL * np.abs(ref) + TIE_ABS * (float(np.max(np.abs(ref))) if ref.size else 0.0)
+    big = float(np.max(np.abs(ref))) if ref.size else 0.0
+    t = TIE_REL * np.abs(ref) + TIE_ABS * big
     tie = (g == numerics.round_to_bf16(ref - t)) | (g == numerics.round_to_bf16(ref + t))
     denom = np.linalg.norm(r)
-    e2 = np.where(tie, 0.0, err)
+    e2 = np.where(tie, 0.0, np.abs(g - r))
     rel = float(np.linalg.norm(e2) / denom) if denom > 0 else float(np.linalg.norm(e2))
-    if not err.size:
+    if not g.size:
         return 0.0, rel, 0.0
-    allow = np.maximum(TOL_MAX_ABS, numerics.bf16_ulp(r))
+    err = np.abs(g - ref)
+    allow = np.maximum(TOL_MAX_ABS, 0.5 * numerics.bf16_ulp(ref) + t)
     return float(np.max(err)), rel, float(np.max(err / allow))
 
 
@@ -106,7 +110,7 @@ class PagedCase:
         self.table_t = torch.from_numpy(self.table).to(DEV)
         self.max_ctx = int(self.lens.max()) if len(self.lens) else 0
         self.offs = W.offsets(self.lens)
-        slots = kvd.slot_mapping_for(self.table_t, self.lens_t)
+        slots = kvd.kvd_slot_mapping(self.table_t, self.lens_t)
         keep = set(range(self.L)) if keep_layers is None else set(keep_layers)
         self.keep_seqs = None if keep_seqs is None else sorted(set(int(i) for i in keep_seqs))
         self.q, self.kv, self.kv_seq = {}, {}, {}

@@ -165,10 +165,39 @@ def test_binding_checks_shapes_before_any_call():
         kvd.make_args(q, bt, lens, 64, out, score=torch.zeros((b + 1, 64)))
     with pytest.raises(ValueError, match="GPU"):         # host tensors never reach the library
         kvd.make_args(q, bt, lens, 64, out)
-    with pytest.raises(ValueError, match="one context length"):
-        kvd.slot_mapping_for(bt, torch.zeros((3,), dtype=torch.int32))
-    with pytest.raises(ValueError, match="longer"):
-        kvd.slot_mapping_for(bt, torch.tensor([65, 1], dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU"):         # the slot mapping is computed on the device
+        kvd.kvd_slot_mapping(bt, lens)
+    with pytest.raises(ValueError, match="block_table"):
+        kvd.kvd_slot_mapping(bt[0], lens)
+
+
+def test_slot_mapping_argument_errors():
+    # (block_table, max_blocks, b, lens, first, out_start, max_tokens, slots, n_slots, stream)
+    assert _status("kvd_slot_mapping", FAKE, 4, -1, FAKE, None, FAKE, 64, FAKE, 64, None) == 1
+    assert _status("kvd_slot_mapping", FAKE, 0, 2, FAKE, None, FAKE, 64, FAKE, 64, None) == 1
+    assert _status("kvd_slot_mapping", FAKE, 4, 2, FAKE, None, FAKE, -1, FAKE, 64, None) == 1
+    assert _status("kvd_slot_mapping", FAKE, 4, 2, FAKE, None, FAKE, 64, FAKE, -1, None) == 1
+    assert _status("kvd_slot_mapping", FAKE, 1 << 27, 2, FAKE, None, FAKE, 64, FAKE, 64, None) == 2
+    assert _status("kvd_slot_mapping", FAKE, 1 << 20, 1 << 16, FAKE, None, FAKE, 1 << 16, FAKE, 64, None) == 2
+    assert _status("kvd_slot_mapping", None, 4, 2, FAKE, None, FAKE, 64, FAKE, 64, None) == 1
+    assert _status("kvd_slot_mapping", FAKE, 4, 2, None, None, FAKE, 64, FAKE, 64, None) == 1
+    assert _status("kvd_slot_mapping", FAKE, 4, 2, FAKE, None, None, 64, FAKE, 64, None) == 1
+    assert _status("kvd_slot_mapping", FAKE, 4, 2, FAKE, None, FAKE, 64, None, 64, None) == 1
+    # nothing to do: no pointer is needed
+    assert _status("kvd_slot_mapping", None, 4, 0, None, None, None, 64, None, 0, None) == 0
+    assert _status("kvd_slot_mapping", None, 4, 2, None, None, None, 0, None, 0, None) == 0
+
+
+def test_unit_map_argument_errors():
+    pool = _pool()
+    args = kvd.DecodeArgs(2, 8, 4, 64, FAKE, FAKE, FAKE, FAKE, None, 0, None, 0, None, 0, 0.0)
+    assert _status("kvd_debug_unit_map", None, ctypes.byref(args), FAKE, None) == 1
+    assert _status("kvd_debug_unit_map", pool.handle, None, FAKE, None) == 1
+    assert _status("kvd_debug_unit_map", pool.handle, ctypes.byref(args), None, None) == 1
+    bad = kvd.DecodeArgs(2, 7, 4, 64, FAKE, FAKE, FAKE, FAKE, None, 0, None, 0, None, 0, 0.0)
+    assert _status("kvd_debug_unit_map", pool.handle, ctypes.byref(bad), FAKE, None) == 1
+    empty = kvd.DecodeArgs(0, 8, 4, 64, None, None, None, None, None, 0, None, 0, None, 0, 0.0)
+    assert _status("kvd_debug_unit_map", pool.handle, ctypes.byref(empty), None, None) == 0
 
 
 def test_write_and_merge_argument_errors():

@@ -110,3 +110,50 @@ def test_fused_append_with_scores(env, fp8):
         assert torch.equal(res[0][0].view(torch.int16), res[1][0].view(torch.int16))
         assert torch.equal(res[0][1], res[1][1])
         assert torch.equal(ref_pool.kv, fused_pool.kv)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_fused_append_past_the_bound_stores_nothing(env, fp8):
+    """A context length above min(max_context_len, 16 * max_blocks_per_seq)
+    has no slot for its new token inside the bound: the call stores nothing
+    (every cached row keeps its bytes) and attends to the clamped context,
+    exactly as the plain decode call with the same arguments."""
+    kvd, H, W, torch = env
+    d = 64
+    lens = np.array([40, 64, 100], dtype=np.int32)
+    w = W.DecodeWorkload("append-fused-bound", seed=75, b=3, layers=1, n_q=4, n_kv=2, head_dim=d,
+                         ctx=("fixed", 0), kv_dtype="fp8" if fp8 else "bf16")
+    table, nb = W.block_tables(w, lens, pad_value=-1)
+    case = H.PagedCase(w, lens=lens, table=table, num_blocks=nb)
+    g = torch.Generator(device="cuda").manual_seed(76)
+    new_k = torch.randn((3, 2, d), generator=g, device="cuda").to(torch.bfloat16)
+    new_v = torch.randn((3, 2, d), generator=g, device="cuda").to(torch.bfloat16)
+    # bound 48: sequence 0 (40 tokens) appends at row 39; 1 and 2 lie past the bound
+    bound = 48
+    ref_pool, fused_pool = _twin(kvd, torch, case), _twin(kvd, torch, case)
+    first = torch.tensor([39, 0, 0], dtype=torch.int32, device="cuda")
+    only0 = torch.tensor([40, 0, 0], dtype=torch.int32, device="cuda")
+    slots = kvd.kvd_slot_mapping(case.table_t, only0, first_token=first)      # sequence 0's token 39 only
+    assert slots.numel() == 1
+    kvd.kvd_write_kv(ref_pool, 0, new_k[:1], new_v[:1], slots)
+    outs = []
+    for pool, fused in ((ref_pool, False), (fused_pool, True)):
+        out = torch.empty_like(case.q[0])
+        lse = torch.empty(case.q[0].shape[:2], dtype=torch.float32, device="cuda")
+        kvd.decode(pool, 0, case.q[0], case.table_t, case.lens_t, bound, out=out, lse_out=lse, chunk_tokens=16,
+                   new_k=new_k if fused else None, new_v=new_v if fused else None)
+        outs.append((out, lse))
+    torch.cuda.synchronize()
+    assert torch.equal(ref_pool.kv, fused_pool.kv)
+    if fp8:
+        assert torch.equal(ref_pool.scales.view(torch.int32), fused_pool.scales.view(torch.int32))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1])
+    # the oracle over the clamped contexts (the stored rows of sequences 1 and 2 unchanged)
+    from oracle import attention
+    qf = H.bf16_to_f64(case.q[0])
+    for i in (1, 2):
+        Ki, Vi = case.logical(0, i)
+        o, _ = attention.decode_sequence(qf[i], Ki[:bound], Vi[:bound])
+        H.assert_bf16_close(outs[1][0][i], o, rel_tol=H.TOL_FP8_REL_L2 if fp8 else H.TOL_REL_L2,
+                            what=f"clamped sequence {i}")

@@ -127,7 +127,7 @@ def test_write_fp8_codes_and_scales_bit_exact(env, d):
     Vf[int(case.offs[5]):int(case.offs[5]) + 16, 0, :] *= 1e-30      # very small magnitudes
     K2, V2 = Kf.to(torch.bfloat16), Vf.to(torch.bfloat16)
     case.kv[0] = (K2, V2)
-    slots = kvd.slot_mapping_for(case.table_t, case.lens_t)
+    slots = kvd.kvd_slot_mapping(case.table_t, case.lens_t)
     kvd.kvd_write_kv(case.pool, 0, K2.cuda(), V2.cuda(), slots)
     torch.cuda.synchronize()
     got = case.pool.kv.cpu().numpy()
@@ -426,3 +426,39 @@ def test_chunk_major_order_edges(env, b):
     ref_o, ref_l = case.oracle(0)
     H.assert_bf16_close(out, ref_o, what=f"chunk-major b={b}")
     H.assert_lse_close(lse, ref_l)
+
+
+def test_slot_mapping_bit_exact(env):
+    """kvd_slot_mapping against the page's rule written out independently:
+    token t of sequence i sits in physical block table[i][t // 16], row t % 16
+    -- on the block-table example of the PagedAttention paragraph (requests A,
+    B, C over 11 blocks) and on a seeded ragged batch with a run of new
+    tokens per sequence, negative entries and empty sequences."""
+    kvd, H, W, torch = env
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "block_table_example.json")) as fh:
+        ex = json.load(fh)
+    rows = [ex["tables"][k] for k in sorted(ex["tables"])]
+    mb = max(len(r) for r in rows)
+    table = np.full((len(rows), mb), -1, dtype=np.int32)
+    for i, r in enumerate(rows):
+        table[i, :len(r)] = r
+    rng = np.random.default_rng(91)
+    lens = np.array([16 * len(r) - int(rng.integers(0, 16)) for r in rows], dtype=np.int32)
+    cases = [(table, lens, None)]
+    b, mb = 37, 50
+    table = rng.permutation(b * mb).astype(np.int32).reshape(b, mb)
+    table[rng.random((b, mb)) < 0.1] = -1
+    lens = rng.integers(0, 16 * mb + 1, size=b).astype(np.int32)
+    lens[:3] = [0, 1, 16 * mb]
+    first = (lens * rng.random(b)).astype(np.int32)
+    cases += [(table, lens, None), (table, lens, first), (table, lens, np.maximum(lens - 1, 0))]
+    for table, lens, first in cases:
+        f = np.zeros_like(lens) if first is None else first
+        want = []
+        for i in range(len(lens)):
+            for t in range(int(f[i]), int(lens[i])):
+                e = int(table[i, t // 16])
+                want.append(-1 if e < 0 else e * 16 + t % 16)
+        got = kvd.kvd_slot_mapping(torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda(),
+                                   None if first is None else torch.from_numpy(first).cuda())
+        assert np.array_equal(got.cpu().numpy(), np.array(want, dtype=np.int32))

@@ -1,0 +1,95 @@
+"""The decode grid's work decomposition, read back from the device.
+
+kvd_debug_unit_map runs the decode kernels' own unit-location code and reports
+the (sequence, chunk) unit of every workgroup.  For each KV head the units
+must cover every (sequence, chunk) pair of the launch exactly once, in the
+order the kernels promise: the chunks a sequence fills completely first, then
+each sequence's partly filled last chunk, then the empty chunks; the full
+chunks chunk-major (chunk c of every sequence that has it, then chunk c + 1)
+when 1 < b <= 512 and there are at most 64 chunks, sequence by sequence
+otherwise.  The order only decides which workgroup computes a unit; the
+batch sizes here reach every branch of the location code (one sequence per
+lane, up to eight, more than eight, more than 64 per lane; more than 64
+chunks).
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import decode_attention_paged_04_amd as kvd
+    return kvd, torch
+
+
+def expected_order(lens, chunk, n_chunks, bound):
+    """Units (sequence, chunk) in grid order, written from the rule above."""
+    s = np.clip(np.asarray(lens, dtype=np.int64), 0, bound)
+    b = len(s)
+    full = [(i, c) for i in range(b) for c in range(n_chunks) if (c + 1) * chunk <= s[i]]
+    if 1 < b <= 512 and n_chunks <= 64:
+        full.sort(key=lambda u: (u[1], u[0]))
+    part = [(i, int(s[i] // chunk)) for i in range(b) if s[i] % chunk]
+    empty = [(i, c) for i in range(b) for c in range(n_chunks) if c * chunk >= s[i]]
+    return full + part + empty, s
+
+
+def _case(kvd, torch, lens, n_kv, chunk, max_ctx, g=2, d=64):
+    b = len(lens)
+    pool = kvd.allocate_pool(1, 1, n_kv, d)
+    mb = max(1, -(-max_ctx // 16))
+    q = torch.zeros((b, g * n_kv, d), dtype=torch.bfloat16, device="cuda")
+    table = torch.zeros((b, mb), dtype=torch.int32, device="cuda")
+    lens_t = torch.tensor(np.asarray(lens, dtype=np.int32), device="cuda")
+    out = torch.empty_like(q)
+    args = kvd.make_args(q, table, lens_t, max_ctx, out, chunk_tokens=chunk, pool=pool)
+    ch, nc = kvd.kvd_decode_plan(pool, args)
+    units = kvd.kvd_debug_unit_map(pool, args).cpu().numpy()
+    return units, ch, nc
+
+
+def _check(units, lens, n_kv, chunk, n_chunks, bound):
+    order, s = expected_order(lens, chunk, n_chunks, bound)
+    assert units.shape == (len(lens) * n_kv * n_chunks, 3)
+    for j in range(n_kv):
+        got = units[j::n_kv]
+        assert got.shape[0] == len(order)
+        exp = np.array(order, dtype=np.int64).reshape(-1, 2)
+        bad = np.nonzero((got[:, 0] != exp[:, 0]) | (got[:, 1] != exp[:, 1]))[0]
+        assert bad.size == 0, f"head {j}: first mismatch at unit {bad[0]}: got {got[bad[0]]}, want {exp[bad[0]]}"
+        assert np.array_equal(got[:, 2], s[exp[:, 0]])
+
+
+CASES = [
+    # (name, b, length range, n_kv, chunk, max_ctx)
+    ("one sequence", 1, (0, 40000), 8, 0, 40000),
+    ("one sequence, 80 chunks", 1, (1280, 1280), 2, 16, 1280),
+    ("3 seqs, 69 chunks (sequence-major)", 3, (1000, 1100), 2, 16, 1100),
+    ("40 seqs, 69 chunks", 40, (0, 1100), 1, 16, 1100),
+    ("64 seqs (one per lane)", 64, (0, 700), 2, 48, 700),
+    ("65 seqs (two per lane)", 65, (0, 700), 2, 48, 700),
+    ("512 seqs (eight per lane)", 512, (0, 300), 1, 16, 300),
+    ("513 seqs (nine per lane)", 513, (0, 300), 1, 16, 300),
+    ("600 seqs", 600, (0, 400), 2, 16, 400),
+    ("600 seqs, 70 chunks", 600, (0, 1120), 1, 16, 1120),
+    ("4095 seqs", 4095, (0, 200), 1, 16, 200),
+    ("4200 seqs (more than 64 per lane)", 4200, (0, 200), 2, 16, 200),
+    ("9000 seqs", 9000, (0, 100), 1, 32, 100),
+    ("lengths above the bound", 100, (0, 5000), 1, 256, 3000),
+]
+
+
+@pytest.mark.parametrize("name,b,rng_lens,n_kv,chunk,max_ctx", CASES, ids=[c[0] for c in CASES])
+def test_unit_map_is_the_promised_order(env, name, b, rng_lens, n_kv, chunk, max_ctx):
+    kvd, torch = env
+    rng = np.random.default_rng(b * 7919 + max_ctx)
+    lens = rng.integers(rng_lens[0], rng_lens[1] + 1, size=b)
+    # empty, one-token and exactly-full sequences among them
+    if b >= 4:
+        lens[0], lens[1], lens[2] = 0, 1, min(max_ctx, 16 * (max(chunk, 16) // 16) * 2)
+    units, ch, nc = _case(kvd, torch, lens, n_kv, chunk, max_ctx)
+    _check(units, lens, n_kv, ch, nc, min(max_ctx, 16 * max(1, -(-max_ctx // 16))))
