@@ -62,6 +62,7 @@ EXPORTS = {
                               ctypes.c_void_p),
     "kvd_decode_attn_append": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs), ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p),
+    "kvd_decode_attn_no_alloc": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs), ctypes.c_void_p),
     "kvd_decode_partials": (ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeArgs), ctypes.c_void_p,
                             ctypes.c_void_p, ctypes.c_void_p),
     "kvd_merge_partials": (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -330,6 +331,13 @@ def kvd_decode_attn_append(pool: Pool, layer: int, args: DecodeArgs, new_k, new_
     _check_tensor(new_v, "new_v", shape, torch.bfloat16, new_k.device)
     _check(lib.kvd_decode_attn_append(pool.handle, layer, ctypes.byref(args), _ptr(new_k), _ptr(new_v),
                                       _stream(stream)), "kvd_decode_attn_append")
+
+
+def kvd_decode_attn_no_alloc(pool: Pool, layer: int, args: DecodeArgs, stream=None):
+    """kvd_decode_attn (bf16 or FP8 pool) with the library's fixed per-device
+    scratch instead of ``args.workspace``: allocates nothing."""
+    _check(lib.kvd_decode_attn_no_alloc(pool.handle, layer, ctypes.byref(args), _stream(stream)),
+           "kvd_decode_attn_no_alloc")
 
 
 def kvd_decode_attn_mixed(pool_bf16: Pool, pool_fp8: Pool, layer: int, args: DecodeArgs, stream=None):

@@ -1,5 +1,7 @@
 // C ABI of libkvdecode: validation, pool layout, launch planning, workspace.
+#include <atomic>
 #include <cstdio>
+#include <mutex>
 #include <new>
 
 #include "kvd_internal.h"
@@ -114,14 +116,49 @@ kvd_status plan_decode(const PoolView& p, const kvd_decode_args* a, DecodePlan* 
   return KVD_OK;
 }
 
+// Scratch of kvd_decode_attn_no_alloc, for callers that cannot allocate: one
+// array per device, held from the library's first use on a device until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it is a stand-in, not device memory); it uses the address
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept in g_scratch.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the calling thread's current device.
+kvd_status static_scratch(char** out) {
+  int dev = -1;
+  KVD_TRY_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return KVD_ERR_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      KVD_TRY_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+      if (!p) return KVD_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = static_cast<char*>(p);
+  return KVD_OK;
+}
+
 // One decode call.  ext_part_o / ext_part_lse (both or neither): write the
 // per-chunk partials there and stop, instead of producing the merged output.
 // pool8 (mixed precision only): the FP8 pool beside the bf16 pool `pool`.
 // new_k / new_v (both or neither): the fused append of token s_i - 1.
+// fixed_ws (with capacity fixed_cap): scratch to use instead of the caller's
+// workspace (args->workspace is then ignored).
 kvd_status decode_common(const kvd_pool* pool, int32_t layer, const kvd_decode_args* a,
                          void* stream, bool any_dtype, kvd_dtype want, float* ext_part_o,
                          float* ext_part_lse, const kvd_pool* pool8 = nullptr,
-                         const void* new_k = nullptr, const void* new_v = nullptr) {
+                         const void* new_k = nullptr, const void* new_v = nullptr,
+                         char* fixed_ws = nullptr, size_t fixed_cap = 0) {
   if (!pool || !a) return KVD_ERR_INVALID_ARG;
   const PoolView& p = pool->v;
   if (!any_dtype && p.dtype != want) return KVD_ERR_DTYPE;
@@ -142,13 +179,15 @@ kvd_status decode_common(const kvd_pool* pool, int32_t layer, const kvd_decode_a
   if (a->b == 0) return KVD_OK;
   if (!a->q || !a->block_table || !a->context_lens) return KVD_ERR_INVALID_ARG;
   if (!external && !a->out) return KVD_ERR_INVALID_ARG;
-  if (!external && pl.total > 0) {
+  if (fixed_ws) {
+    if (pl.total > fixed_cap) return KVD_ERR_WORKSPACE;
+  } else if (!external && pl.total > 0) {
     if (!a->workspace || a->workspace_bytes < pl.total) return KVD_ERR_WORKSPACE;
     if (((uintptr_t)a->workspace & 255) != 0) return KVD_ERR_WORKSPACE;
   }
   if (external && ((((uintptr_t)ext_part_o) & 15) != 0 || (((uintptr_t)ext_part_lse) & 3) != 0))
     return KVD_ERR_INVALID_ARG;
-  char* ws = static_cast<char*>(a->workspace);
+  char* ws = fixed_ws ? fixed_ws : static_cast<char*>(a->workspace);
   const bool final_direct = !external && pl.final_direct;
   kvd::DecodeLaunch L{};
   L.layer_base = p.kv_base + (size_t)layer * (size_t)p.layer_bytes;
@@ -321,6 +360,20 @@ kvd_status kvd_decode_attn_append(const kvd_pool* pool, int32_t layer, const kvd
                                   const void* new_k, const void* new_v, void* hip_stream) {
   if (!new_k || !new_v) return KVD_ERR_INVALID_ARG;
   return decode_common(pool, layer, args, hip_stream, true, KVD_BF16, nullptr, nullptr, nullptr, new_k, new_v);
+}
+
+kvd_status kvd_decode_attn_no_alloc(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
+                                    void* hip_stream) {
+  if (!pool || !args) return KVD_ERR_INVALID_ARG;
+  DecodePlan pl;
+  kvd_status st = plan_decode(pool->v, args, &pl);
+  if (st != KVD_OK) return st;
+  if (pl.total > kStaticScratchBytes) return KVD_ERR_WORKSPACE;   // before any HIP call
+  char* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != KVD_OK) return st;
+  return decode_common(pool, layer, args, hip_stream, true, KVD_BF16, nullptr, nullptr, nullptr, nullptr, nullptr,
+                       ws, kStaticScratchBytes);
 }
 
 kvd_status kvd_decode_partials(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,

@@ -15,7 +15,8 @@
  *
  * Ownership.  Every device buffer is allocated, owned and freed by the
  * caller.  The library never allocates or frees device memory and keeps no
- * mutable global state.  A pool handle holds host metadata only; it is
+ * mutable global state, with one exception: the fixed per-device scratch of
+ * kvd_decode_attn_no_alloc.  A pool handle holds host metadata only; it is
  * immutable after creation and may be shared by threads and streams.
  * Buffers must stay alive until the stream work that uses them completes.
  *
@@ -282,6 +283,24 @@ kvd_status kvd_decode_attn_append(const kvd_pool* pool, int32_t layer, const kvd
  * not bf16 or pool_fp8 not FP8. */
 kvd_status kvd_decode_attn_mixed(const kvd_pool* pool_bf16, const kvd_pool* pool_fp8, int32_t layer,
                                  const kvd_decode_args* args, void* hip_stream);
+
+/* kvd_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same step, on a bf16 or an FP8 pool alike (the pool's dtype picks the
+ * kernels, as in kvd_decode_attn_append), with the split partials and score
+ * scratch kept in a fixed array the library holds on each device (32 MiB,
+ * the first call on a device looks up its address; it stays allocated until
+ * the process ends) instead of args->workspace, which is ignored.  Calls
+ * whose kvd_decode_workspace_bytes exceeds 32 MiB return KVD_ERR_WORKSPACE
+ * before any launch.  The call itself allocates nothing.  Every call on one
+ * device uses that device's one array: calls that overlap in time on the same
+ * device (on different streams, or from different threads) race and give
+ * undefined results; calls in order on one stream are safe.  The stream must
+ * belong to the calling thread's current device.  Nothing in the array has to
+ * start at any value.  Outputs, lse and score equal those of kvd_decode_attn /
+ * kvd_decode_attn_fp8 with a workspace, bit for bit. */
+kvd_status kvd_decode_attn_no_alloc(const kvd_pool* pool, int32_t layer, const kvd_decode_args* args,
+                                    void* hip_stream);
 
 /* Per-chunk partial results of one decode step of one layer, for a caller
  * that merges them itself -- for example the partials of context shards held
