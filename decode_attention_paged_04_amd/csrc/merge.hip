@@ -7,8 +7,14 @@
 
 namespace kvd {
 
-constexpr float kLog2eMerge = 1.4426950408889634f;
-constexpr int kMergeThreads = 256;
+// Log-sum-exp merge of one (sequence, query head)'s per-chunk partials by one
+// wave: lse = M + ln(sum_c exp(lse_c - M)) with M = max_c lse_c (lane l takes
+// chunks l, l + 64, ...; the lanes' values are combined by butterfly
+// shuffles), out = sum_c exp(lse_c - lse) * o_c added in chunk order and
+// rounded to bf16.  A chunk whose weight is 0 (lse_c = -inf: nothing
+// attended) adds nothing and its o_c is never used, so it may hold anything,
+// NaN included; no chunk with weight gives out = 0 and lse = -inf.
+constexpr float kMergeLog2e = 1.4426950408889634f;
 
 __device__ inline float wave_max(float v) {
 #pragma unroll
@@ -22,150 +28,82 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-// Splits of more than kFewChunks chunks (see merge_few_kernel below): one
-// workgroup of four waves per (sequence, query head); wave w owns the channels
-// [w*D/4, (w+1)*D/4).  lse = M + ln(sum_c exp(lse_c - M)) with M = max_c
-// lse_c over all n_chunks chunks; out = sum_c exp(lse_c - lse) * o_c, rounded
-// to bf16.  The o_c of a chunk whose weight is 0 (lse_c = -inf) is
-// loaded but never used, so it may hold anything, NaN included.  No chunk, or
-// only empty ones: out = 0, lse = -inf.
-// Every wave computes M and the sum itself with shuffles (no LDS, no
-// barrier), and all loads of a batch of up to kBatch chunks per lane are
-// issued before any is used, so a merge of a few dozen chunks costs about one
-// memory round trip.  Lane l of a wave takes channel l % (D/4) and the chunks
-// c = l / (D/4) (mod NG), NG = 256 / D; the NG partial sums of a channel are
-// added with shuffles in a fixed order.
-template <int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_lse, int32_t n_chunks,
-    uint16_t* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ lse2) {
-  constexpr int CH = D / 4;                      // channels per wave
-  constexpr int NG = 64 / CH;                    // chunk groups per channel
-  constexpr int kBatch = 16;                     // chunks per lane loaded at once
-  const size_t ih = blockIdx.x;
-  // Chunks past a sequence's end, or with nothing attended, carry lse -inf:
-  // they weigh 0, so no context length has to be read before the loads go out.
-  const int nc = n_chunks;
-  const float* pl = part_lse + ih * n_chunks;
-  const float* po = part_o + ih * n_chunks * D;
+// po: o_c rows [nc][D]; pl: lse_c [nc] (natural log).  Writes out[0 .. D)
+// (bf16), *lse_out and *lse2 (log2 domain) when given.  Lane l owns channels
+// l, l + 64, ...; up to BATCH chunks' outputs are loaded before any is used.
+template <int D, int BATCH>
+__device__ inline void merge_head(const float* __restrict__ po, const float* __restrict__ pl, int nc,
+                                  uint16_t* __restrict__ out, float* lse_out, float* lse2) {
+  constexpr int PER = D / 64;
   const int lane = threadIdx.x & 63;
-  const int ch = (threadIdx.x >> 6) * CH + lane % CH;
-  const int grp = lane / CH;
-
-  // first batch of this lane's partial outputs, loaded before the reductions
-  float ov[kBatch];
+  float ov[BATCH][PER];
 #pragma unroll
-  for (int k = 0; k < kBatch; ++k) {
-    const int c = grp + k * NG;
-    ov[k] = c < nc ? po[(size_t)c * D + ch] : 0.f;
-  }
-  // lane c holds lse_c of the first 64 chunks; more chunks are looped over
+  for (int k = 0; k < BATCH; ++k)
+#pragma unroll
+    for (int p = 0; p < PER; ++p) ov[k][p] = k < nc ? po[(size_t)k * D + lane + 64 * p] : 0.f;
   const float lv = lane < nc ? pl[lane] : -INFINITY;
   float mx = lv;
   for (int c = lane + 64; c < nc; c += 64) mx = fmaxf(mx, pl[c]);
   const float M = wave_max(mx);
   if (M == -INFINITY) {
-    if (grp == 0) out[ih * D + ch] = 0;
-    if (threadIdx.x == 0) {
-      if (lse_out) lse_out[ih] = -INFINITY;
-      if (lse2) lse2[ih] = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) out[lane + 64 * p] = 0;
+    if (lane == 0) {
+      if (lse_out) *lse_out = -INFINITY;
+      if (lse2) *lse2 = -INFINITY;
     }
     return;
   }
   float sm = lane < nc ? expf(lv - M) : 0.f;
   for (int c = lane + 64; c < nc; c += 64) sm += expf(pl[c] - M);
   const float lse = M + logf(wave_sum(sm));
-  // each lane's weight exp(lse_c - lse) for c = lane, shared by shuffles below
-  const float wl = lane < nc ? expf(lv - lse) : 0.f;
-
-  float acc = 0.f;
-#pragma unroll
-  for (int k = 0; k < kBatch; ++k) {
-    const int c = grp + k * NG;                    // < 64: its weight sits in lane c
-    const float w = __shfl(wl, c);
-    if (c < nc && w != 0.f) acc += w * ov[k];
-  }
-  for (int c0 = kBatch * NG; c0 < nc; c0 += kBatch * NG) {   // long splits: further batches
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int c = c0 + grp + k * NG;
-      ov[k] = c < nc ? po[(size_t)c * D + ch] : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int c = c0 + grp + k * NG;
-      if (c < nc) {
-        const float w = expf(pl[c] - lse);
-        if (w != 0.f) acc += w * ov[k];
-      }
-    }
-  }
-#pragma unroll
-  for (int off = CH; off < 64; off <<= 1) acc += __shfl_xor(acc, off);
-  if (grp == 0) out[ih * D + ch] = float_to_bf16_bits(acc);
-  if (threadIdx.x == 0) {
-    if (lse_out) lse_out[ih] = lse;
-    if (lse2) lse2[ih] = lse * kLog2eMerge;
-  }
-}
-
-// The same merge for splits of at most kFewChunks chunks, one wave per
-// (sequence, query head) and four heads per workgroup: with many heads and few
-// chunks (a large batch of short contexts) a workgroup per head would make
-// the launch mostly workgroup dispatch.  Lane l takes channels l, l + 64, ...
-// and all the chunks; lane c holds lse_c.  All partial outputs are loaded
-// before the reductions, and each channel's sum runs in chunk order.
-constexpr int kFewChunks = 16;
-
-template <int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_few_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_lse, int64_t n_heads,
-    int32_t n_chunks, uint16_t* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ lse2) {
-  constexpr int PER = D / 64;                    // channels per lane
-  const int lane = threadIdx.x & 63;
-  const int64_t ih = (int64_t)blockIdx.x * (kMergeThreads / 64) + (threadIdx.x >> 6);
-  if (ih >= n_heads) return;                     // the whole wave
-  const int nc = n_chunks;                       // 1 .. kFewChunks
-  const float* pl = part_lse + ih * nc;
-  const float* po = part_o + ih * nc * D + lane;
-  float ov[kFewChunks][PER];
-#pragma unroll
-  for (int c = 0; c < kFewChunks; ++c)
-#pragma unroll
-    for (int p = 0; p < PER; ++p) ov[c][p] = c < nc ? po[(size_t)c * D + 64 * p] : 0.f;
-  const float lv = lane < nc ? pl[lane] : -INFINITY;
-  const float M = wave_max(lv);
-  uint16_t* o = out + ih * D + lane;
-  if (M == -INFINITY) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) o[64 * p] = 0;
-    if (lane == 0) {
-      if (lse_out) lse_out[ih] = -INFINITY;
-      if (lse2) lse2[ih] = -INFINITY;
-    }
-    return;
-  }
-  const float lse = M + logf(wave_sum(lane < nc ? expf(lv - M) : 0.f));
-  const float wl = lane < nc ? expf(lv - lse) : 0.f;
+  const float wl = lane < nc ? expf(lv - lse) : 0.f;   // weight of chunk `lane` (< 64)
   float acc[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) acc[p] = 0.f;
+  for (int c0 = 0; c0 < nc; c0 += BATCH) {               // uniform
+    if (c0 > 0) {
 #pragma unroll
-  for (int c = 0; c < kFewChunks; ++c) {
-    if (c < nc) {                                // uniform
-      const float w = __shfl(wl, c);
-      if (w != 0.f) {                            // uniform: an empty chunk's o_c is never used
+      for (int k = 0; k < BATCH; ++k)
 #pragma unroll
-        for (int p = 0; p < PER; ++p) acc[p] += w * ov[c][p];
+        for (int p = 0; p < PER; ++p)
+          ov[k][p] = c0 + k < nc ? po[(size_t)(c0 + k) * D + lane + 64 * p] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int c = c0 + k;
+      if (c < nc) {                                      // uniform
+        const float w = c < 64 ? __shfl(wl, c) : expf(pl[c] - lse);
+        if (w != 0.f) {                                  // uniform: an empty chunk's o_c is never used
+#pragma unroll
+          for (int p = 0; p < PER; ++p) acc[p] += w * ov[k][p];
+        }
       }
     }
   }
 #pragma unroll
-  for (int p = 0; p < PER; ++p) o[64 * p] = float_to_bf16_bits(acc[p]);
+  for (int p = 0; p < PER; ++p) out[lane + 64 * p] = float_to_bf16_bits(acc[p]);
   if (lane == 0) {
-    if (lse_out) lse_out[ih] = lse;
-    if (lse2) lse2[ih] = lse * kLog2eMerge;
+    if (lse_out) *lse_out = lse;
+    if (lse2) *lse2 = lse * kMergeLog2e;
   }
+}
+
+// One wave per (sequence, query head), four heads per workgroup: with many
+// heads and few chunks (a large batch of short contexts) a workgroup per head
+// would make the launch mostly workgroup dispatch.  merge_head loads up to
+// BATCH chunks' outputs before it uses any, so a split of up to BATCH chunks
+// costs about one memory round trip.
+constexpr int kMergeThreads = 256;
+
+template <int D, int BATCH>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, int64_t n_heads,
+    int32_t n_chunks, uint16_t* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ lse2) {
+  const int64_t ih = (int64_t)blockIdx.x * (kMergeThreads / 64) + (threadIdx.x >> 6);
+  if (ih >= n_heads) return;                     // the whole wave
+  merge_head<D, BATCH>(part_o + ih * n_chunks * D, part_lse + ih * n_chunks, n_chunks, out + ih * D,
+                       lse_out ? lse_out + ih : nullptr, lse2 ? lse2 + ih : nullptr);
 }
 
 // Slot of token t in the score scratch.  Within each 32-token pair the decode
@@ -216,24 +154,24 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ lo
 hipError_t launch_merge(const float* part_o, const float* part_lse, int32_t b, int32_t n_q,
                         int32_t n_chunks, int32_t head_dim, uint16_t* out, float* lse_out,
                         float* lse2, hipStream_t stream) {
-  if (n_chunks <= kFewChunks) {
-    const int64_t heads = (int64_t)b * n_q;
-    const dim3 grid((unsigned)((heads + kMergeThreads / 64 - 1) / (kMergeThreads / 64)));
-    if (head_dim == 128)
-      hipLaunchKernelGGL(merge_few_kernel<128>, grid, dim3(kMergeThreads), 0, stream, part_o, part_lse, heads,
-                         n_chunks, out, lse_out, lse2);
+  const int64_t heads = (int64_t)b * n_q;
+  const dim3 grid((unsigned)((heads + kMergeThreads / 64 - 1) / (kMergeThreads / 64)));
+  const dim3 block(kMergeThreads);
+  if (head_dim == 128) {
+    if (n_chunks <= 16)
+      hipLaunchKernelGGL((merge_kernel<128, 16>), grid, block, 0, stream, part_o, part_lse, heads, n_chunks, out,
+                         lse_out, lse2);
     else
-      hipLaunchKernelGGL(merge_few_kernel<64>, grid, dim3(kMergeThreads), 0, stream, part_o, part_lse, heads,
-                         n_chunks, out, lse_out, lse2);
-    return hipGetLastError();
+      hipLaunchKernelGGL((merge_kernel<128, 32>), grid, block, 0, stream, part_o, part_lse, heads, n_chunks, out,
+                         lse_out, lse2);
+  } else {
+    if (n_chunks <= 16)
+      hipLaunchKernelGGL((merge_kernel<64, 16>), grid, block, 0, stream, part_o, part_lse, heads, n_chunks, out,
+                         lse_out, lse2);
+    else
+      hipLaunchKernelGGL((merge_kernel<64, 32>), grid, block, 0, stream, part_o, part_lse, heads, n_chunks, out,
+                         lse_out, lse2);
   }
-  const dim3 grid((unsigned)((size_t)b * n_q));
-  if (head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, part_o, part_lse,
-                       n_chunks, out, lse_out, lse2);
-  else
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, stream, part_o, part_lse,
-                       n_chunks, out, lse_out, lse2);
   return hipGetLastError();
 }
 

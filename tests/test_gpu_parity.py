@@ -249,8 +249,11 @@ def test_merge_partials_export(env, nc, d):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("chunk", [0, 48, 128])
+@pytest.mark.parametrize("chunk", [0, 16, 48, 128])
 def test_decode_partials_match_oracle_chunks(env, fp8, chunk):
+    """Per-chunk partials against the oracle's, and their merge against the
+    one-call result bit for bit (16, 48 and 128 tokens: 63, 21 and 8 chunks;
+    0: the library's chunking, one chunk here)."""
     kvd, H, W, torch = env
     from oracle import attention
     w = _workload(W, 8, 128, fp8=fp8, seed=700)
@@ -462,3 +465,48 @@ def test_slot_mapping_bit_exact(env):
         got = kvd.kvd_slot_mapping(torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda(),
                                    None if first is None else torch.from_numpy(first).cuda())
         assert np.array_equal(got.cpu().numpy(), np.array(want, dtype=np.int32))
+
+
+def test_workspace_reused_across_shapes(env):
+    """One workspace serves calls of different shapes in turn (batch, heads,
+    chunking, scores), twice round: each call's outputs, lse and scores equal
+    those of the same call on a fresh workspace, bit for bit -- nothing a call
+    leaves in the workspace reaches a later call."""
+    kvd, H, W, torch = env
+    shapes = [  # (b, n_q, n_kv, d, length range, chunk, score)
+        (6, 16, 4, 128, (100, 3000), 128, False),
+        (20, 8, 2, 64, (1, 900), 32, True),
+        (2, 32, 8, 128, (2000, 4000), 256, False),
+        (40, 8, 4, 128, (0, 700), 64, False),
+        (3, 8, 2, 64, (1, 300), 32, True),
+    ]
+    cases = []
+    for k, (b, n_q, n_kv, d, span, chunk, with_score) in enumerate(shapes):
+        w = W.DecodeWorkload(f"ws-reuse-{k}", seed=500 + k, b=b, layers=1, n_q=n_q, n_kv=n_kv, head_dim=d,
+                             ctx=("uniform", span[0], span[1]))
+        cases.append((H.PagedCase(w), chunk, with_score))
+    need = 0
+    for case, chunk, with_score in cases:
+        score = torch.zeros((case.w.b, case.max_ctx), device="cuda") if with_score else None
+        a = kvd.make_args(case.q[0], case.table_t, case.lens_t, case.max_ctx, torch.empty_like(case.q[0]),
+                          chunk_tokens=chunk, score=score, score_weight=0.5, pool=case.pool)
+        need = max(need, kvd.kvd_decode_workspace_bytes(case.pool, a))
+    shared = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    for rnd in range(2):
+        for k, (case, chunk, with_score) in enumerate(cases):
+            res = []
+            for ws in (shared, None):
+                q = case.q[0]
+                out = torch.full_like(q, float("nan"))
+                lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+                score = torch.ones((case.w.b, case.max_ctx), device="cuda") if with_score else None
+                kvd.decode(case.pool, 0, q, case.table_t, case.lens_t, case.max_ctx, out=out, lse_out=lse,
+                           chunk_tokens=chunk, score=score, score_weight=0.5, workspace=ws)
+                res.append((out, lse, score))
+            torch.cuda.synchronize()
+            (o1, l1, s1), (o2, l2, s2) = res
+            assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), (rnd, k)
+            assert torch.equal(l1, l2), (rnd, k)
+            if with_score:
+                assert torch.equal(s1, s2), (rnd, k)
+            assert not torch.isnan(o1.float()).any(), (rnd, k)
