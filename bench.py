@@ -366,42 +366,127 @@ def measured_traffic(workload: str):
     return float(m_b.group(1))
 
 
-def cpu_baseline(wl: Workload, budget_s: float):
-    """The float64 oracle as it stands, timed on the host on a bounded sample."""
+def host_threads():
+    """(os.cpu_count(), CPUs in this process's affinity mask, BLAS threads)."""
+    aff = len(os.sched_getaffinity(0))
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [0]) or None
+    except Exception:
+        pass
+    return os.cpu_count(), aff, blas
+
+
+def measured_l2(workload: str):
+    """L2 hit rate and L2 read requests per launch from the committed rocprofv3
+    counter summary of a workload, if it was taken on the current decode kernel
+    source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_l2_counters.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"decode kernel source digest:\s*`?([0-9a-f]+)", txt)
+    m_hit = re.search(r"L2 hit rate:\s*([0-9.]+)", txt)
+    m_rd = re.search(r"L2 read bytes per launch:\s*([0-9.eE+]+)", txt)
+    if not m_src or not m_hit or m_src.group(1) != source_digest():
+        return None
+    return {"hit_rate": float(m_hit.group(1)), "read_bytes_per_launch": float(m_rd.group(1)) if m_rd else None}
+
+
+def cpu_baseline(w, lens, budget_s: float):
+    """The float64 oracle as it stands, timed on the host on a bounded sample of
+    the workload: every sequence of the first layer and of the last layer (the
+    one layer of a one-layer workload, repeated), sequence by sequence until each
+    layer's share of the budget is spent; FP8 pools time the decoding of the
+    stored codes too, a fused score the score increment.  The rate is the
+    algorithmic bytes of the sampled (layer, sequence) units over their time;
+    seq-steps/s extrapolates the sampled layers' time per byte to the whole step.
+    BLAS threads are set to the CPUs of this process's affinity mask."""
     import numpy as np
     import torch
     import workloads as W
-    from oracle import attention, numerics
+    from oracle import attention, e4m3, scores
+    from threadpoolctl import threadpool_limits
 
-    def f64(t):
-        return numerics.bf16_bits_to_f64(t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+    def fp8_codes(x):
+        """E4M3 codes [s][n_kv][d] (uint8) and per-(block, KV head) scales of a
+        bf16 sequence -- input for timing the oracle's decoding, made with
+        torch's cast (quicker than the oracle's own quantiser)."""
+        s_, n_kv, d = x.shape
+        nb = -(-s_ // 16)
+        t = torch.zeros((nb * 16, n_kv, d), dtype=torch.float32)
+        t[:s_] = x.float()
+        t = t.view(nb, 16, n_kv, d)
+        sc = t.abs().amax(dim=(1, 3)) / 448.0
+        y = (t / torch.where(sc == 0, torch.ones_like(sc), sc)[:, None, :, None]).clamp(-448, 448)
+        codes = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(nb * 16, n_kv, d)[:s_]
+        return codes.numpy(), sc.numpy()
 
-    w = wl.w
-    i = 0
-    s = int(wl.lens[i])
-    K, V = W.keys_values(w, 0, int(wl.lens.sum()), "cuda")
-    Kf, Vf = f64(K[:s]), f64(V[:s])
-    del K, V
-    qf = f64(wl.q[0])[i]
-    try:
+    fp8 = w.kv_dtype == "fp8"
+    kvb = 1 if fp8 else 2
+    cpu_count, aff, _ = host_threads()
+    sample_layers = [0] if w.layers == 1 else [0, w.layers - 1]
+    per_layer_budget = budget_s / len(sample_layers)
+    offs = W.offsets(lens)
+    n_tok = int(offs[-1])
+    P = w.shared_prefix
+    done_bytes, secs, units, reps_total = 0, 0.0, 0, 0
+    layer_bytes = algorithmic_step_bytes(lens, 1, w.n_q, w.n_kv, w.head_dim, kvb, fp8, False)
+    with threadpool_limits(limits=aff):
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        attention.decode_sequence(qf, Kf, Vf)
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = (time.perf_counter() - t0) / reps
-    seq_layer_bytes = algorithmic_step_bytes([s], 1, w.n_q, w.n_kv, w.head_dim, wl.kv_bytes, wl.fp8, False)
-    return {"value": round(seq_layer_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": (f"oracle decode of sequence {i} for one layer ({w.n_q} query heads, s={s}, "
-                       f"float64 numpy) repeated {reps}x in {reps * dt:.1f}s; host cores visible: "
-                       f"{len(os.sched_getaffinity(0))}"),
-            "seq_layer_steps_per_s": round(1.0 / dt, 3)}
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [0]) or None
+        dev = "cuda" if torch.cuda.is_available() else "cpu"
+        for layer in sample_layers:
+            K, V = W.keys_values(w, layer, n_tok, dev)
+            Kc, Vc = K.cpu(), V.cpu()
+            del K, V
+            qf = W.query(w, layer, dev).cpu().to(torch.float64).numpy()
+            spent = 0.0
+            for i, s in enumerate(lens):
+                a, e = int(offs[i]), int(offs[i + 1])
+                if P and i:                         # the shared prompt is stored once, by sequence 0
+                    Ki, Vi = torch.cat([Kc[:P], Kc[a + P:e]]), torch.cat([Vc[:P], Vc[a + P:e]])
+                else:
+                    Ki, Vi = Kc[a:e], Vc[a:e]
+                # inputs in the oracle's form (bf16 -> float64 is exact); not timed
+                Kf, Vf = Ki.to(torch.float64).numpy(), Vi.to(torch.float64).numpy()
+                if fp8:                             # stored codes and scales of the sequence
+                    ck, sk = fp8_codes(Ki)
+                    cv, sv = fp8_codes(Vi)
+                reps, t0 = 0, time.perf_counter()
+                while True:
+                    if fp8:
+                        Kd, Vd = e4m3.dequantize_sequence(ck, sk), e4m3.dequantize_sequence(cv, sv)
+                    else:
+                        Kd, Vd = Kf, Vf
+                    attention.decode_sequence(qf[i], Kd, Vd)
+                    if w.scores and int(s):
+                        scores.layer_increment(attention.attention_weights_sequence(qf[i], Kd), 1.0 / w.layers)
+                    reps += 1
+                    # a one-sequence layer is repeated to fill its budget
+                    if len(lens) > 1 or time.perf_counter() - t0 >= per_layer_budget:
+                        break
+                dt = time.perf_counter() - t0
+                secs += dt
+                spent += dt
+                units += 1
+                reps_total += reps
+                done_bytes += reps * algorithmic_step_bytes([s], 1, w.n_q, w.n_kv, w.head_dim, kvb, fp8, False)
+                if spent >= per_layer_budget:
+                    break
+    rate = done_bytes / secs                        # bytes per second of oracle time
+    step_s = w.layers * layer_bytes / rate + (8 * int(np.sum(lens)) / rate if w.scores else 0.0)
+    full = units * 1 >= len(lens) * len(sample_layers)
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": int(aff), "kind": "oracle",
+            "os_cpu_count": cpu_count, "affinity_cpus": aff, "blas_threads": blas,
+            "sample": (f"float64 numpy oracle (decode{' + FP8 decoding' if fp8 else ''}"
+                       f"{' + score increment' if w.scores else ''}) on {units} (layer, sequence) units of "
+                       f"layers {sample_layers} ({reps_total} calls, {secs:.1f} s)"
+                       + ("" if full else ", the first sequences of each layer until its budget was spent")
+                       + (f"; extrapolated to all {w.layers} layers" if w.layers > 1 else "")),
+            "extrapolated": w.layers > 1 or not full,
+            "seq_steps_per_s": round(len(lens) / step_s, 4)}
 
 
 def measure(name: str, chunk: int, replicas: int, steps: int, warmup: int, launches: int):
@@ -421,9 +506,14 @@ def measure(name: str, chunk: int, replicas: int, steps: int, warmup: int, launc
     return wl, res
 
 
-def extra_entry(name: str, steps: int):
-    """A further workload in the same line: step rate, kernel roofline, and for a
-    shared prefix the rate over the bytes actually stored (each shared block once)."""
+def extra_entry(name: str, steps: int, cpu_seconds: float = 0.0):
+    """A further workload in the same line: step rate, kernel roofline, the
+    oracle baseline and, for a shared prefix, the rates over the bytes actually
+    stored (each shared block once).  A shared prefix's blocks are read by every
+    request but fetched from HBM about once (the requests behind it read them
+    together, from L2), so its roofline is taken over the unique stored bytes --
+    what HBM has to deliver -- and the rate over every request's logical bytes
+    is reported beside it."""
     wl, r = measure(name, 0, 0, steps, 2, 40)
     e = {"workload": r["config"]["workload"], "value": round(r["value"], 2), "unit": "GB/s",
          "ms_per_step": round(r["ms_per_step"], 4), "steps": steps,
@@ -433,9 +523,20 @@ def extra_entry(name: str, steps: int):
                       "frac": round(r["achieved"] / PEAK_HBM_GBS, 4), "traffic": measured_traffic(name),
                       "launch_us": round(r["launch_us"], 2)}}
     if wl.w.shared_prefix:
+        unique_launch = wl.unique_step_bytes // wl.w.layers
+        ach = unique_launch / (r["launch_us"] / 1e6) / 1e9
         e["unique_bytes_per_step"] = wl.unique_step_bytes
         e["unique_GBs"] = round(wl.unique_step_bytes / (r["ms_per_step"] / 1e3) / 1e9, 1)
+        e["pct_of_hbm_peak"] = round(100.0 * e["unique_GBs"] / PEAK_HBM_GBS, 2)
+        e["logical_GBs"] = e["value"]
+        e["roofline"].update({"basis": "unique stored bytes (each shared block once)", "achieved": round(ach, 2),
+                              "frac": round(ach / PEAK_HBM_GBS, 4), "bytes_per_launch": unique_launch,
+                              "logical_GBs": round(r["achieved"], 2), "l2": measured_l2(name)})
+    w, lens = wl.w, wl.lens
     wl.free()
+    if cpu_seconds > 0:
+        e["cpu_baseline"] = cpu_baseline(w, lens, cpu_seconds)
+        log(f"{name} cpu baseline: {e['cpu_baseline']['value']} GB/s ({e['cpu_baseline']['sample']})")
     return e
 
 
@@ -645,7 +746,9 @@ def main():
     ap.add_argument("--no-append", action="store_true", help="skip the append-cost entries")
     ap.add_argument("--no-tiered", action="store_true", help="skip the tier-restricted entry")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-precision entry")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle budget of the headline entry")
+    ap.add_argument("--extra-cpu-seconds", type=float, default=6.0,
+                    help="oracle budget of each further entry (two layers, extrapolated)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration) and exit")
@@ -678,16 +781,18 @@ def main():
         return
 
     wl, head = measure(args.workload, args.chunk, args.replicas, args.steps, args.warmup, args.launches)
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
-        log(f"cpu baseline: {cpu['value']} GB/s on {cpu['cores']} thread(s)")
+    w_head, lens_head = wl.w, wl.lens
     wl.free()
     del wl
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w_head, lens_head, args.cpu_seconds)
+        log(f"cpu baseline: {cpu['value']} GB/s on {cpu['cores']} thread(s) ({cpu['sample']})")
 
     secondary = None
     if args.secondary != "none" and args.secondary != args.workload:
         wl2, sec = measure(args.secondary, 0, 0, args.secondary_steps, 2, 80)
+        w2, lens2 = wl2.w, wl2.lens
         wl2.free()
         del wl2
         traffic2 = measured_traffic(args.secondary)
@@ -699,11 +804,15 @@ def main():
                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                   "frac": round(sec["achieved"] / PEAK_HBM_GBS, 4),
                                   "traffic": traffic2, "launch_us": round(sec["launch_us"], 2)}}
+        if not args.no_cpu_baseline:
+            secondary["cpu_baseline"] = cpu_baseline(w2, lens2, args.extra_cpu_seconds)
+            log(f"secondary cpu baseline: {secondary['cpu_baseline']['value']} GB/s "
+                f"({secondary['cpu_baseline']['sample']})")
 
     extras = []
     if args.extras != "none":
         for name in args.extras.split(","):
-            extras.append(extra_entry(name, 10))
+            extras.append(extra_entry(name, 10, 0.0 if args.no_cpu_baseline else args.extra_cpu_seconds))
     tiered = None
     if not args.no_tiered:
         tiered = tiered_entry("8b_ragged", 8, 10)
