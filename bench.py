@@ -102,11 +102,9 @@ class Workload:
         dev = "cuda"
         self.lens_t = torch.from_numpy(self.lens).to(dev)
         self.table_t = torch.from_numpy(self.table).to(dev)
-        slots = kvd.kvd_slot_mapping(self.table_t, self.lens_t)
-        n_tok = int(self.lens.sum())
-        offs = W.offsets(self.lens)
-        for i in range(1, w.b):                 # a shared prefix is stored once, by sequence 0
-            slots[int(offs[i]):int(offs[i]) + w.shared_prefix] = -1
+        # a shared prefix is stored once, by sequence 0: rows are generated for the stored tokens only
+        first, _, n_tok = W.stored_rows(w, self.lens)
+        slots = kvd.kvd_slot_mapping(self.table_t, self.lens_t, first_token=torch.from_numpy(first).to(dev))
         self.unique_step_bytes = self.step_bytes - w.layers * (w.b - 1) * w.shared_prefix * (
             2 * w.n_kv * w.head_dim * self.kv_bytes)
         dt = kvd.KVD_FP8_E4M3 if self.fp8 else kvd.KVD_BF16
@@ -428,8 +426,7 @@ def cpu_baseline(w, lens, budget_s: float):
     cpu_count, aff, _ = host_threads()
     sample_layers = [0] if w.layers == 1 else [0, w.layers - 1]
     per_layer_budget = budget_s / len(sample_layers)
-    offs = W.offsets(lens)
-    n_tok = int(offs[-1])
+    _, start, n_tok = W.stored_rows(w, lens)
     P = w.shared_prefix
     done_bytes, secs, units, reps_total = 0, 0.0, 0, 0
     layer_bytes = algorithmic_step_bytes(lens, 1, w.n_q, w.n_kv, w.head_dim, kvb, fp8, False)
@@ -444,11 +441,12 @@ def cpu_baseline(w, lens, budget_s: float):
             qf = W.query(w, layer, dev).cpu().to(torch.float64).numpy()
             spent = 0.0
             for i, s in enumerate(lens):
-                a, e = int(offs[i]), int(offs[i + 1])
+                a = int(start[i])
                 if P and i:                         # the shared prompt is stored once, by sequence 0
-                    Ki, Vi = torch.cat([Kc[:P], Kc[a + P:e]]), torch.cat([Vc[:P], Vc[a + P:e]])
+                    e = a + int(s) - P
+                    Ki, Vi = torch.cat([Kc[:P], Kc[a:e]]), torch.cat([Vc[:P], Vc[a:e]])
                 else:
-                    Ki, Vi = Kc[a:e], Vc[a:e]
+                    Ki, Vi = Kc[a:a + int(s)], Vc[a:a + int(s)]
                 # inputs in the oracle's form (bf16 -> float64 is exact); not timed
                 Kf, Vf = Ki.to(torch.float64).numpy(), Vi.to(torch.float64).numpy()
                 if fp8:                             # stored codes and scales of the sequence
@@ -741,7 +739,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="chunk_tokens (0 = the library's choice)")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas (0 = enough to exceed the cache)")
     ap.add_argument("--launches", type=int, default=200, help="event-timed launches for the roofline")
-    ap.add_argument("--extras", default="8b_ragged,8b_fp8_scores,70b_shard,8b_prefix,8b_prefix256,8b_batch256",
+    ap.add_argument("--extras", default="8b_ragged,8b_fp8_scores,70b_shard,8b_prefix,8b_prefix256,8b_prefix1024,"
+                    "8b_batch256",
                     help="further workloads reported in the same line (comma list), or 'none'")
     ap.add_argument("--no-append", action="store_true", help="skip the append-cost entries")
     ap.add_argument("--no-tiered", action="store_true", help="skip the tier-restricted entry")

@@ -68,9 +68,9 @@ __device__ inline int qk_channel0(int c, int G) { return 32 * c + 8 * G; }
 // b * n_chunks units, n_chunks covering the longest allowed context, but a
 // sequence of s tokens fills only ceil(s / chunk) of its chunks.  Workgroup x
 // takes KV head x % n_kv and unit k = x / n_kv of this order, in three runs:
-// the full chunks (chunk-major when 1 < b <= 512 and n_chunks <= 64, else
-// sequence by sequence), then the partly filled last chunks, then the empty
-// chunks, sequence by sequence.  The hardware hands out workgroups in grid
+// the full chunks chunk-major (chunk 0 of every sequence that has it, in
+// sequence order, then chunk 1, ...), then the partly filled last chunks, then
+// the empty chunks, sequence by sequence.  The hardware hands out workgroups in grid
 // order, so the shorter units run last and the final workgroups drain sooner;
 // an empty chunk only marks itself empty for the merge (or writes a zero
 // output), and at the end of the grid such workgroups no longer hold compute
@@ -138,13 +138,13 @@ __device__ inline Unit locate_unit(const DecodeLaunch& a, int k) {
     const int full = sl / a.chunk;
     return run == 0 ? 0 : (run == 1 ? full : full + (sl % a.chunk != 0 ? 1 : 0));
   };
-  if (per == 1) {                                      // lane l owns just sequence l
-    if (run == 0 && a.b > 1 && a.n_chunks <= 64) {
-      // Full chunks chunk-major: chunk c of every sequence that has it, in
-      // sequence order, then chunk c + 1.  Sequences that share prefix blocks
-      // then read them together, from one XCD's L2 (the workgroups of one KV
-      // head share an XCD).  The order only decides which workgroup computes
-      // a unit, never its arithmetic.
+  if (run == 0 && a.b > 1) {
+    // Full chunks chunk-major: chunk c of every sequence that has it, in
+    // sequence order, then chunk c + 1.  Sequences that share prefix blocks
+    // then read them together, from one XCD's L2 (the workgroups of one KV
+    // head share an XCD).  The order only decides which workgroup computes a
+    // unit, never its arithmetic.
+    if (per == 1 && a.n_chunks <= 64) {                // lane l owns just sequence l
       int kr = kk, c = 0;
       for (;;) {                                       // uniform; ends since kk < n_full
         const uint64_t m = __ballot(nf > c);
@@ -158,21 +158,24 @@ __device__ inline Unit locate_unit(const DecodeLaunch& a, int k) {
         ++c;
       }
     }
-    const int sl = __shfl(s1, li);
-    return Unit{li, first_of(sl) + kq, sl};
-  }
-  if (run == 0 && per <= 8 && a.n_chunks <= 64) {
-    // The same chunk-major order over several sequences per lane.  F(c), the
-    // number of full chunks with index below c, is found by a wave sum; a
-    // binary search gives the chunk index c with F(c) <= kk < F(c + 1), then
-    // a prefix sum over the lanes and a walk over the owning lane's sequences
-    // give the (kk - F(c))-th sequence that has chunk c.
-    auto F = [&](int c) {
+    // Any b and chunk count: F(c), the number of full chunks with index below
+    // c, is a wave sum (over the lane's counts kept in nfs when it owns at
+    // most eight sequences, else recounted from their lengths); a binary
+    // search gives the chunk index c with F(c) <= kk < F(c + 1), then a prefix
+    // sum over the lanes and a walk over the owning lane's sequences give the
+    // (kk - F(c))-th sequence that has chunk c.
+    auto below = [&](int c) {                          // this lane's full chunks with index < c
       int t = 0;
+      if (per <= 8) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) t += min(nfs[m], c);
-      return __builtin_amdgcn_readfirstlane(__shfl(wave_inclusive_sum(t), 63));
+        for (int m = 0; m < 8; ++m) t += min(nfs[m], c);
+      } else {
+#pragma unroll 8
+        for (int m = 0; m < per; ++m) t += min(length(lane * per + m) / a.chunk, c);
+      }
+      return t;
     };
+    auto F = [&](int c) { return __builtin_amdgcn_readfirstlane(__shfl(wave_inclusive_sum(below(c)), 63)); };
     int lo_c = 0, hi_c = a.n_chunks;                   // F(lo_c) <= kk < F(hi_c) = n_full
     while (hi_c - lo_c > 1) {
       const int mid = (lo_c + hi_c) >> 1;
@@ -181,23 +184,42 @@ __device__ inline Unit locate_unit(const DecodeLaunch& a, int k) {
     }
     const int c = lo_c;
     const int kr = kk - F(c);
-    int cl = 0;
+    int cl = 0;                                        // this lane's sequences that have chunk c
+    if (per <= 8) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) cl += nfs[m] > c ? 1 : 0;
+      for (int m = 0; m < 8; ++m) cl += nfs[m] > c ? 1 : 0;
+    } else {
+#pragma unroll 8
+      for (int m = 0; m < per; ++m) cl += length(lane * per + m) / a.chunk > c ? 1 : 0;
+    }
     const int inc = wave_inclusive_sum(cl);
     const int l2 = __popcll(__ballot(inc <= kr));
     int r = __builtin_amdgcn_readfirstlane(kr - __shfl(inc - cl, l2));
+    if (per <= 8) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int v = __builtin_amdgcn_readfirstlane(__shfl(nfs[m], l2));
-      if (m < per && v > c) {
-        if (r == 0) {
-          const int q = l2 * per + m;
-          return Unit{q, c, length(q)};
+      for (int m = 0; m < 8; ++m) {
+        const int v = __builtin_amdgcn_readfirstlane(__shfl(nfs[m], l2));
+        if (m < per && v > c) {
+          if (r == 0) {
+            const int q = l2 * per + m;
+            return Unit{q, c, length(q)};
+          }
+          --r;
         }
-        --r;
+      }
+    } else {
+      for (int m = 0; m < per; ++m) {                  // uniform
+        const int q = l2 * per + m;
+        if (__builtin_amdgcn_readfirstlane(length(q) / a.chunk) > c) {
+          if (r == 0) return Unit{q, c, length(q)};
+          --r;
+        }
       }
     }
+  }
+  if (per == 1) {                                      // lane l owns just sequence l
+    const int sl = __shfl(s1, li);
+    return Unit{li, first_of(sl) + kq, sl};
   }
   for (int m0 = 0; m0 < per; m0 += 64) {
     const int q = li * per + m0 + lane;

@@ -123,39 +123,49 @@ def test_full_8b_fp8_with_scores(env):
         assert err <= H.TOL_SCORE_REL
 
 
-def test_full_shared_prefix_batch(env):
-    """The shared-prefix workload the benchmark times (32 requests behind one
-    16,384-token prompt stored once, 1,024 own tokens each; one layer, the
-    library's chunking, whose full chunks run chunk-major): sampled sequences
+@pytest.mark.parametrize("name,chunks", [("8b_prefix", (0,)), ("8b_prefix1024", (0, 512))])
+def test_full_shared_prefix_batch(env, name, chunks):
+    """The shared-prefix workloads the benchmark times (32 requests behind one
+    16,384-token prompt, 1,024 behind one 4,096-token prompt; the prompt stored
+    once, each request's own tokens after it; one layer): sampled sequences
     against the oracle over each one's logical K/V -- the prompt's rows as
-    stored by request 0, then its own."""
+    stored by request 0, then its own -- with the library's chunking and, for
+    the 1,024 requests, 512-token chunks (nine per request, chunk-major over
+    sixteen sequences per lane)."""
     kvd, H, W, torch = env
     from oracle import attention
-    w = W.WORKLOADS["8b_prefix"].with_(layers=1)
+    w = W.WORKLOADS[name].with_(layers=1)
     lens = W.context_lengths(w)
     table, nb = W.block_tables(w, lens)
-    offs = W.offsets(lens)
-    n = int(offs[-1])
+    first, start, n = W.stored_rows(w, lens)
     table_t, lens_t = torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda()
-    slots = kvd.kvd_slot_mapping(table_t, lens_t)
-    for i in range(1, w.b):                          # the prompt is stored once, by request 0
-        slots[int(offs[i]):int(offs[i]) + w.shared_prefix] = -1
+    slots = kvd.kvd_slot_mapping(table_t, lens_t, first_token=torch.from_numpy(first).cuda())
+    assert slots.numel() == n
     pool = kvd.allocate_pool(1, nb, w.n_kv, w.head_dim, kvd.KVD_BF16)
     K, V = W.keys_values(w, 0, n, "cuda")
     kvd.kvd_write_kv(pool, 0, K, V, slots)
     q = W.query(w, 0, "cuda")
-    out = torch.empty_like(q)
-    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
-    kvd.decode(pool, 0, q, table_t, lens_t, int(lens.max()), out=out, lse_out=lse)
-    torch.cuda.synchronize()
     qf = H.bf16_to_f64(q)
     Kc, Vc = K.cpu(), V.cpu()
+    del K, V
     P = w.shared_prefix
-    for i in (0, 13, 31):
-        a, e = int(offs[i]), int(offs[i + 1])
-        Ki = torch.cat([Kc[:P], Kc[a + P:e]]) if i else Kc[a:e]
-        Vi = torch.cat([Vc[:P], Vc[a + P:e]]) if i else Vc[a:e]
-        ref_o, ref_l = attention.decode_sequence(qf[i], H.bf16_to_f64(Ki), H.bf16_to_f64(Vi))
-        mx, rel = H.assert_bf16_close(out[i], ref_o, what=f"shared prefix seq {i}")
-        H.say(f"shared prefix seq {i}: max-abs {mx:.2e} rel-L2 {rel:.2e}")
-        H.assert_lse_close(lse[i:i + 1], ref_l[None])
+    rng = np.random.default_rng(w.seed + 5)
+    sample = sorted({0, 13, w.b - 1, int(rng.integers(1, w.b - 1))})
+    refs = {}
+    for i in sample:
+        a = int(start[i])
+        e = a + int(lens[i]) - (P if i else 0)
+        Ki = torch.cat([Kc[:P], Kc[a:e]]) if i else Kc[a:e]
+        Vi = torch.cat([Vc[:P], Vc[a:e]]) if i else Vc[a:e]
+        refs[i] = attention.decode_sequence(qf[i], H.bf16_to_f64(Ki), H.bf16_to_f64(Vi))
+    for chunk in chunks:
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+        kvd.decode(pool, 0, q, table_t, lens_t, int(lens.max()), out=out, lse_out=lse, chunk_tokens=chunk)
+        torch.cuda.synchronize()
+        for i in sample:
+            ref_o, ref_l = refs[i]
+            mx, rel = H.assert_bf16_close(out[i], ref_o, what=f"{name} chunk {chunk} seq {i}")
+            H.say(f"{name} chunk {chunk} seq {i}: max-abs {mx:.2e} rel-L2 {rel:.2e}")
+            H.assert_lse_close(lse[i:i + 1], ref_l[None])
+        assert not torch.isnan(out.float()).any()

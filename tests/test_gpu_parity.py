@@ -409,8 +409,7 @@ def test_tiny_workload(env):
 
 @pytest.mark.parametrize("b", [2, 64, 65, 150, 512])
 def test_chunk_major_order_edges(env, b):
-    """The chunk-major order of full chunks (1 < b <= 512, n_chunks <= 64) at
-    its edges: one sequence per lane (b <= 64, lane 63 owning the last) and up
+    """The chunk-major order of full chunks at its edges: one sequence per lane (b <= 64, lane 63 owning the last) and up
     to eight (65, 150, 512), exactly 64 chunks of 16 tokens, sequences with no
     full chunk, with every chunk full, and empty ones.  Every unit must be computed once: outputs and lse against the
     oracle."""

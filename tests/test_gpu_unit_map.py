@@ -5,12 +5,11 @@ the (sequence, chunk) unit of every workgroup.  For each KV head the units
 must cover every (sequence, chunk) pair of the launch exactly once, in the
 order the kernels promise: the chunks a sequence fills completely first, then
 each sequence's partly filled last chunk, then the empty chunks; the full
-chunks chunk-major (chunk c of every sequence that has it, then chunk c + 1)
-when 1 < b <= 512 and there are at most 64 chunks, sequence by sequence
-otherwise.  The order only decides which workgroup computes a unit; the
-batch sizes here reach every branch of the location code (one sequence per
-lane, up to eight, more than eight, more than 64 per lane; more than 64
-chunks).
+chunks chunk-major (chunk c of every sequence that has it, then chunk c + 1),
+the other two runs sequence by sequence.  The order only decides which
+workgroup computes a unit; the batch sizes here reach every branch of the
+location code (one sequence per lane, up to eight, more than eight, more than
+64 per lane; more than 64 chunks).
 """
 import numpy as np
 import pytest
@@ -31,8 +30,7 @@ def expected_order(lens, chunk, n_chunks, bound):
     s = np.clip(np.asarray(lens, dtype=np.int64), 0, bound)
     b = len(s)
     full = [(i, c) for i in range(b) for c in range(n_chunks) if (c + 1) * chunk <= s[i]]
-    if 1 < b <= 512 and n_chunks <= 64:
-        full.sort(key=lambda u: (u[1], u[0]))
+    full.sort(key=lambda u: (u[1], u[0]))
     part = [(i, int(s[i] // chunk)) for i in range(b) if s[i] % chunk]
     empty = [(i, c) for i in range(b) for c in range(n_chunks) if c * chunk >= s[i]]
     return full + part + empty, s
@@ -68,7 +66,7 @@ CASES = [
     # (name, b, length range, n_kv, chunk, max_ctx)
     ("one sequence", 1, (0, 40000), 8, 0, 40000),
     ("one sequence, 80 chunks", 1, (1280, 1280), 2, 16, 1280),
-    ("3 seqs, 69 chunks (sequence-major)", 3, (1000, 1100), 2, 16, 1100),
+    ("3 seqs, 69 chunks", 3, (1000, 1100), 2, 16, 1100),
     ("40 seqs, 69 chunks", 40, (0, 1100), 1, 16, 1100),
     ("64 seqs (one per lane)", 64, (0, 700), 2, 48, 700),
     ("65 seqs (two per lane)", 65, (0, 700), 2, 48, 700),

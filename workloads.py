@@ -78,6 +78,10 @@ WORKLOADS = {
     "8b_prefix256": DecodeWorkload("llama3.1-8b-8layer-b256-shared8k+512", seed=9, b=256, layers=8,
                                    n_q=32, n_kv=8, head_dim=128, ctx=("fixed", 8704),
                                    shared_prefix=8192),
+    # 1,024 requests behind one 4,096-token system prompt
+    "8b_prefix1024": DecodeWorkload("llama3.1-8b-8layer-b1024-shared4k+256", seed=10, b=1024, layers=8,
+                                    n_q=32, n_kv=8, head_dim=128, ctx=("fixed", 4352),
+                                    shared_prefix=4096),
     # a large serving batch: 256 requests of 1k..4k tokens
     "8b_batch256": DecodeWorkload("llama3.1-8b-32layer-b256-s1k..4k", seed=8, b=256, layers=32,
                                   n_q=32, n_kv=8, head_dim=128, ctx=("uniform", 1024, 4096)),
@@ -176,6 +180,29 @@ def keys_values(w: DecodeWorkload, layer: int, n_tokens: int, device="cpu"):
         k.mul_(ck)
         v.mul_(cv)
     return k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+def stored_rows(w: DecodeWorkload, lens: np.ndarray):
+    """Where the rows generated for a batch sit when a shared prefix is stored
+    once: sequence 0's rows (the shared prompt, then its own), then every other
+    sequence's own rows, in sequence order.
+
+    Returns ``(first, start, n_rows)``: the first stored token of each sequence
+    (0 for sequence 0, the prefix length for the others), the row at which each
+    sequence's stored tokens begin, and the number of rows.  Without a shared
+    prefix this is ``(0, offsets[:-1], offsets[-1])``.  Sequence i's logical
+    rows are rows ``[0, P)`` followed by ``[start[i], start[i] + s_i - P)`` for
+    i >= 1, and ``[0, s_0)`` for i = 0.
+    """
+    lens = np.asarray(lens, dtype=np.int64)
+    P = w.shared_prefix if len(lens) else 0
+    first = np.full(len(lens), P, dtype=np.int32)
+    if len(lens):
+        first[0] = 0
+    stored = lens - first
+    start = np.zeros(len(lens), dtype=np.int64)
+    start[1:] = np.cumsum(stored)[:-1]
+    return first, start, int(stored.sum())
 
 
 def offsets(lens: np.ndarray) -> np.ndarray:
