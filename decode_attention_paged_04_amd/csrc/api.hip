@@ -179,6 +179,9 @@ kvd_status decode_common(const kvd_pool* pool, int32_t layer, const kvd_decode_a
   if (a->b == 0) return KVD_OK;
   if (!a->q || !a->block_table || !a->context_lens) return KVD_ERR_INVALID_ARG;
   if (!external && !a->out) return KVD_ERR_INVALID_ARG;
+  // the kernels' vector accesses: q in 16-byte loads, out in 8-byte stores
+  if (((uintptr_t)a->q & 15) != 0 || (!external && ((uintptr_t)a->out & 7) != 0)) return KVD_ERR_INVALID_ARG;
+  if (((uintptr_t)a->lse_out & 3) != 0 || ((uintptr_t)a->score & 3) != 0) return KVD_ERR_INVALID_ARG;
   if (fixed_ws) {
     if (pl.total > fixed_cap) return KVD_ERR_WORKSPACE;
   } else if (!external && pl.total > 0) {
@@ -389,7 +392,10 @@ kvd_status kvd_merge_partials(const float* part_o, const float* part_lse, int32_
   if (d_h != 64 && d_h != 128) return KVD_ERR_UNSUPPORTED;
   if (b == 0) return KVD_OK;
   if (!part_o || !part_lse || !out_bf16) return KVD_ERR_INVALID_ARG;
-  if ((int64_t)b * n_q >= ((int64_t)1 << 24)) return KVD_ERR_UNSUPPORTED;   // 256-work-item workgroups
+  if (((uintptr_t)part_o & 15) != 0 || ((uintptr_t)part_lse & 3) != 0 || ((uintptr_t)out_bf16 & 7) != 0 ||
+      ((uintptr_t)lse_out & 3) != 0)
+    return KVD_ERR_INVALID_ARG;
+  if ((int64_t)b * n_q >= ((int64_t)1 << 24)) return KVD_ERR_UNSUPPORTED;   // a wave per head at most
   clear_stale_error();
   KVD_TRY_HIP(kvd::launch_merge(part_o, part_lse, b, n_q, n_chunks, d_h, static_cast<uint16_t*>(out_bf16),
                                 lse_out, nullptr, static_cast<hipStream_t>(hip_stream)));

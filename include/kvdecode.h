@@ -176,7 +176,8 @@ typedef struct {
   int32_t n_q;                /* query heads, a multiple of the pool's n_kv           */
   int32_t max_blocks_per_seq; /* row length of block_table                            */
   int32_t max_context_len;    /* host-known bound on every s_i (sizes the launch)     */
-  const void* q;              /* device bf16 [b][n_q][head_dim], post-RoPE            */
+  const void* q;              /* device bf16 [b][n_q][head_dim], post-RoPE, 16-byte   */
+                              /* aligned                                              */
   const int32_t* block_table; /* device int32 [b][max_blocks_per_seq]; entries at or  */
                               /* past ceil(s_i / 16) are never read.  A negative     */
                               /* entry marks a block that is not attended: its tokens */
@@ -188,7 +189,8 @@ typedef struct {
                               /* (the result is then undefined).                     */
   const int32_t* context_lens;/* device int32 [b]; s_i is clamped into               */
                               /* [0, min(max_context_len, 16 * max_blocks_per_seq)]  */
-  void* out;                  /* device bf16 [b][n_q][head_dim]; s_i = 0 gives zeros  */
+  void* out;                  /* device bf16 [b][n_q][head_dim], 8-byte aligned;      */
+                              /* s_i = 0 gives zeros                                  */
   float* lse_out;             /* optional device fp32 [b][n_q]: natural-log           */
                               /* log-sum-exp of the scaled scores (-inf if s_i = 0)   */
   int32_t chunk_tokens;       /* context split: 0 = automatic, else a multiple of 16  */
@@ -325,13 +327,18 @@ kvd_status kvd_decode_partials(const kvd_pool* pool, int32_t layer, const kvd_de
  * lets a long context be split over workgroups or over devices (the
  * capacity-bound sharding of "The KV Cache Is the New Memory Wall" review,
  * Tab. 5) and put together here.
- * part_o:   device fp32 [b][n_q][n_chunks][d_h], each chunk's normalised output
+ * part_o:   device fp32 [b][n_q][n_chunks][d_h], 16-byte aligned, each chunk's
+ *           normalised output
  * part_lse: device fp32 [b][n_q][n_chunks], natural log; -inf marks an empty
- *           chunk, which contributes nothing (its part_o row is never read)
- * out_bf16: device bf16 [b][n_q][d_h]; lse_out: optional fp32 [b][n_q].
+ *           chunk, which contributes nothing (its part_o row may hold anything,
+ *           NaN included)
+ * out_bf16: device bf16 [b][n_q][d_h], 8-byte aligned; lse_out: optional fp32
+ *           [b][n_q].
  * lse = M + ln(sum_c exp(lse_c - M)), M = max_c lse_c, and
- * out = sum_c exp(lse_c - lse) * o_c, rounded to bf16 (nearest even).
- * d_h must be 64 or 128. */
+ * out = sum_c exp(lse_c - lse) * o_c in fp32, rounded to bf16 (nearest even);
+ * the order of the fp32 additions is fixed for given b, n_q, n_chunks and d_h,
+ * so equal inputs give equal bits.  d_h must be 64 or 128 (else
+ * KVD_ERR_UNSUPPORTED); a misaligned or NULL pointer gives KVD_ERR_INVALID_ARG. */
 kvd_status kvd_merge_partials(const float* part_o, const float* part_lse, int32_t b, int32_t n_q,
                               int32_t n_chunks, int32_t d_h, void* out_bf16, float* lse_out,
                               void* hip_stream);

@@ -110,6 +110,8 @@ def _args(**kw):
     (dict(chunk_tokens=16), 4),            # needs a workspace, none given
     (dict(chunk_tokens=16, workspace=FAKE, workspace_bytes=16), 4),
     (dict(chunk_tokens=16, workspace=FAKE + 16, workspace_bytes=1 << 30), 4),   # misaligned
+    (dict(q=FAKE + 8), 1), (dict(out=FAKE + 4), 1),                            # misaligned vectors
+    (dict(lse_out=FAKE + 2), 1), (dict(score=FAKE + 2, score_stride=100), 1),
 ])
 def test_decode_argument_errors(kw, status):
     pool = _pool()
@@ -210,6 +212,11 @@ def test_write_and_merge_argument_errors():
     assert _status("kvd_merge_partials", FAKE, FAKE, 1, 4, 0, 128, FAKE, None, None) == 1
     assert _status("kvd_merge_partials", None, FAKE, 1, 4, 2, 128, FAKE, None, None) == 1
     assert _status("kvd_merge_partials", None, None, 0, 4, 2, 128, None, None, None) == 0
+    # misaligned: part_o (16 bytes), part_lse (4), out (8), lse_out (4)
+    assert _status("kvd_merge_partials", FAKE + 4, FAKE, 1, 4, 2, 128, FAKE, None, None) == 1
+    assert _status("kvd_merge_partials", FAKE, FAKE + 2, 1, 4, 2, 128, FAKE, None, None) == 1
+    assert _status("kvd_merge_partials", FAKE, FAKE, 1, 4, 2, 128, FAKE + 2, None, None) == 1
+    assert _status("kvd_merge_partials", FAKE, FAKE, 1, 4, 2, 128, FAKE, FAKE + 1, None) == 1
     assert _status("kvd_debug_fp8_decode", None, -1, None, None) == 1
     assert _status("kvd_debug_gather_offsets", pool.handle, 0, FAKE, 2, 1, 33, FAKE, FAKE, None) == 1
 

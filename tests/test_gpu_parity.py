@@ -219,17 +219,23 @@ def test_block_placement_and_reruns_are_bit_identical(env):
         assert torch.equal(l, outs[0][1])
 
 
-@pytest.mark.parametrize("nc", [1, 2, 6, 16, 17, 40, 100])
+# (b, n_q, n_chunks): the merge spreads a head over 1 to 8 waves (rows per
+# wave R = 2 .. 16) and holds 1 to 8 rows per lane, looping past 8R chunks.
+# 15 heads: R up to 16, 1 to 8 rows per lane, 300 chunks loop three times;
+# 2,048 heads: one wave per head (two with d_h 64), looping past 16 (32)
+# chunks; 256 heads: R = 8 with one and four rows per lane.
+MERGE_SHAPES = ([(3, 5, nc) for nc in (1, 2, 6, 16, 17, 40, 100, 300)]
+                + [(64, 32, nc) for nc in (2, 5, 16, 40)] + [(8, 32, 8), (8, 32, 24)])
+
+
+@pytest.mark.parametrize("b,n_q,nc", MERGE_SHAPES)
 @pytest.mark.parametrize("d", [64, 128])
-def test_merge_partials_export(env, nc, d):
-    """Both merge kernels (up to 16 chunks: one wave per head, four heads per
-    workgroup -- 15 heads leave the last workgroup part empty; more chunks: a
-    workgroup per head), an empty chunk whose partial holds NaN, and a head
-    with every chunk empty."""
+def test_merge_partials_export(env, b, n_q, nc, d):
+    """Every shape of the merge kernel, an empty chunk whose partial holds NaN,
+    and a head with every chunk empty, against the oracle's merge."""
     kvd, H, W, torch = env
     from oracle import attention
-    rng = np.random.default_rng(5 + nc + d)
-    b, n_q = 3, 5
+    rng = np.random.default_rng(5 + nc + d + 1000 * b)
     part_o = rng.standard_normal((b, n_q, nc, d)).astype(np.float32)
     part_lse = (rng.standard_normal((b, n_q, nc)) * 3).astype(np.float32)
     if nc > 1:
