@@ -126,15 +126,19 @@ class Workload:
         if w.scores:
             self.score0 = W.initial_scores(w, self.max_ctx, dev)
             self.score = self.score0.clone()
+        # a batch behind one shared prompt reads it mostly from the L2: even chunks
+        # (KVD_FLAG_EVEN_CHUNKS), as a caller that knows of the sharing would ask for
+        self.even = w.shared_prefix > 0
+        self.chunk_arg = chunk
         probe = kvd.make_args(self.q[0], self.table_t, self.lens_t, self.max_ctx, self.out[0],
                               chunk_tokens=chunk, score=self.score,
-                              score_weight=1.0 / w.layers, pool=self.pools[0])
+                              score_weight=1.0 / w.layers, pool=self.pools[0], even_chunks=self.even)
         self.chunk, self.n_chunks = kvd.kvd_decode_plan(self.pools[0], probe)
         ws_bytes = kvd.kvd_decode_workspace_bytes(self.pools[0], probe)
         self.ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
         self.args = [[kvd.make_args(self.q[l], self.table_t, self.lens_t, self.max_ctx, self.out[l],
                                     chunk_tokens=chunk, workspace=self.ws, score=self.score,
-                                    score_weight=1.0 / w.layers, pool=self.pools[r])
+                                    score_weight=1.0 / w.layers, pool=self.pools[r], even_chunks=self.even)
                       for l in range(w.layers)] for r in range(self.R)]
         self.fn = kvd.lib.kvd_decode_attn_fp8 if self.fp8 else kvd.lib.kvd_decode_attn
         # the decode kernel on its own: per-chunk partials into separate buffers
@@ -142,7 +146,8 @@ class Workload:
         self.part_o = torch.empty((b, n_q, self.n_chunks, d), dtype=torch.float32, device=dev)
         self.part_lse = torch.empty((b, n_q, self.n_chunks), dtype=torch.float32, device=dev)
         self.pargs = [[kvd.make_args(self.q[l], self.table_t, self.lens_t, self.max_ctx, None,
-                                     chunk_tokens=chunk, pool=self.pools[r], need_out=False)
+                                     chunk_tokens=chunk, pool=self.pools[r], need_out=False,
+                                     even_chunks=self.even)
                        for l in range(w.layers)] for r in range(self.R)]
 
     def call(self, r: int, layer: int, stream: int):
@@ -239,10 +244,12 @@ class Workload:
                              + (2 * w.n_kv * 4 * sum(-(-k // 16) for k in kept_tokens) if self.fp8 else 0))
         self.step_bytes = w.layers * self.launch_bytes
         self.args = [[kvd.make_args(self.q[l], self.table_t, self.lens_t, self.max_ctx, self.out[l],
-                                    chunk_tokens=self.chunk, workspace=self.ws, pool=self.pools[r])
+                                    chunk_tokens=self.chunk_arg, workspace=self.ws, pool=self.pools[r],
+                                    even_chunks=self.even)
                       for l in range(w.layers)] for r in range(self.R)]
         self.pargs = [[kvd.make_args(self.q[l], self.table_t, self.lens_t, self.max_ctx, None,
-                                     chunk_tokens=self.chunk, pool=self.pools[r], need_out=False)
+                                     chunk_tokens=self.chunk_arg, pool=self.pools[r], need_out=False,
+                                     even_chunks=self.even)
                        for l in range(w.layers)] for r in range(self.R)]
 
     def time_append(self, n: int):
@@ -330,7 +337,8 @@ class Workload:
         return {"workload": w.name, "b": w.b, "layers": w.layers, "n_q": w.n_q, "n_kv": w.n_kv,
                 "head_dim": w.head_dim, "context": ctx, "block_size": 16,
                 "kv_dtype": w.kv_dtype, "fused_scores": bool(w.scores), "shared_prefix": w.shared_prefix,
-                "chunk_tokens": self.chunk, "n_chunks": self.n_chunks, "pool_replicas": self.R,
+                "chunk_tokens": self.chunk, "n_chunks": self.n_chunks, "even_chunks": self.even,
+                "pool_replicas": self.R,
                 "num_blocks": self.num_blocks, "hip_graphs": True}
 
     def free(self):

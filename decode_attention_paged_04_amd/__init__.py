@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libkvdecode.so")
 
 BLOCK_SIZE = 16
 KVD_BF16, KVD_FP8_E4M3 = 0, 1
+KVD_FLAG_EVEN_CHUNKS = 1
 STATUS = {0: "KVD_OK", 1: "KVD_ERR_INVALID_ARG", 2: "KVD_ERR_UNSUPPORTED", 3: "KVD_ERR_DTYPE",
           4: "KVD_ERR_WORKSPACE", 5: "KVD_ERR_HIP", 6: "KVD_ERR_CAPACITY"}
 KVD_ERR_CAPACITY = 6
@@ -42,7 +43,7 @@ class DecodeArgs(ctypes.Structure):
                 ("lse_out", ctypes.c_void_p), ("chunk_tokens", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("score", ctypes.c_void_p), ("score_stride", ctypes.c_int32),
-                ("score_weight", ctypes.c_float)]
+                ("score_weight", ctypes.c_float), ("flags", ctypes.c_uint32)]
 
 
 EXPORTS = {
@@ -253,13 +254,13 @@ def _check_tensor(t, name: str, shape, dtype, device=None):
 
 def make_args(q, block_table, context_lens, max_context_len: int, out, lse_out=None,
               chunk_tokens: int = 0, workspace=None, score=None, score_weight: float = 0.0,
-              pool: Optional["Pool"] = None, need_out: bool = True) -> DecodeArgs:
+              pool: Optional["Pool"] = None, need_out: bool = True, even_chunks: bool = False) -> DecodeArgs:
     """Check every tensor against the others (and the pool) and pack the C struct.
 
     The C library sees raw pointers only, so this is where sizes are enforced:
     q ``[b][n_q][d]`` bf16, block_table ``[b][max_blocks]`` int32, context_lens
     ``[b]`` int32, out like q, lse_out ``[b][n_q]`` fp32, score ``[b][stride]`` fp32,
-    all contiguous and on q's device.
+    all contiguous and on q's device.  ``even_chunks`` sets KVD_FLAG_EVEN_CHUNKS.
     """
     import torch
     _require(q is not None and q.dim() == 3, "q must be [b][n_q][head_dim]")
@@ -286,7 +287,8 @@ def make_args(q, block_table, context_lens, max_context_len: int, out, lse_out=N
         b, n_q, int(block_table.shape[1]), int(max_context_len),
         _ptr(q), _ptr(block_table), _ptr(context_lens), _ptr(out), _ptr(lse_out), int(chunk_tokens),
         _ptr(workspace), int(workspace.numel() * workspace.element_size()) if workspace is not None else 0,
-        _ptr(score), int(score.shape[1]) if score is not None else 0, float(score_weight))
+        _ptr(score), int(score.shape[1]) if score is not None else 0, float(score_weight),
+        KVD_FLAG_EVEN_CHUNKS if even_chunks else 0)
 
 
 def kvd_decode_plan(pool: Pool, args: DecodeArgs):
@@ -365,7 +367,8 @@ def decode_mixed(pool_bf16: Pool, pool_fp8: Pool, layer: int, q, block_table, co
 
 
 def kvd_decode_partials(pool: Pool, layer: int, q, block_table, context_lens, max_context_len: int,
-                        part_o=None, part_lse=None, chunk_tokens: int = 0, stream=None):
+                        part_o=None, part_lse=None, chunk_tokens: int = 0, stream=None,
+                        even_chunks: bool = False):
     """Per-chunk partials (fp32 o_c ``[b][n_q][n_chunks][d]``, lse_c ``[b][n_q][n_chunks]``).
 
     Allocates the partial buffers when not given; returns ``(part_o, part_lse, chunk, n_chunks)``.
@@ -373,7 +376,7 @@ def kvd_decode_partials(pool: Pool, layer: int, q, block_table, context_lens, ma
     import torch
     b, n_q, d = (int(x) for x in q.shape)
     args = make_args(q, block_table, context_lens, max_context_len, None, chunk_tokens=chunk_tokens,
-                     pool=pool, need_out=False)
+                     pool=pool, need_out=False, even_chunks=even_chunks)
     chunk, nc = kvd_decode_plan(pool, args)
     if part_o is None:
         part_o = torch.empty((b, n_q, nc, d), dtype=torch.float32, device=q.device)
@@ -416,11 +419,11 @@ def kvd_debug_gather_offsets(pool: Pool, layer: int, block_table, n_tok: int, ou
 
 
 def kvd_debug_unit_map(pool: Pool, args: DecodeArgs, device="cuda", stream=None):
-    """(sequence, chunk, clamped length) of every workgroup of a decode launch
-    with ``args`` (workgroup x serves KV head x % n_kv), int32 ``[grid][3]``."""
+    """(sequence, chunk, clamped length, KV head, first token, end token) of
+    every workgroup of a decode launch with ``args``, int32 ``[grid][6]``."""
     import torch
     _, nc = kvd_decode_plan(pool, args)
-    units = torch.full((int(args.b) * pool.desc.n_kv * nc, 3), -7, dtype=torch.int32, device=device)
+    units = torch.full((int(args.b) * pool.desc.n_kv * nc, 6), -7, dtype=torch.int32, device=device)
     _check(lib.kvd_debug_unit_map(pool.handle, ctypes.byref(args), _ptr(units), _stream(stream)),
            "kvd_debug_unit_map")
     return units
@@ -450,14 +453,14 @@ def kvd_debug_stream_read(data, sink, grid: int, stream=None):
 
 def decode(pool: Pool, layer: int, q, block_table, context_lens, max_context_len: int, out=None,
            lse_out=None, chunk_tokens: int = 0, score=None, score_weight: float = 0.0,
-           workspace=None, stream=None, new_k=None, new_v=None):
+           workspace=None, stream=None, new_k=None, new_v=None, even_chunks: bool = False):
     """Convenience: allocate out/workspace as needed and run one decode call
     (with ``new_k``/``new_v``: the fused append of token s_i - 1 first)."""
     import torch
     if out is None:
         out = torch.empty_like(q)
     args = make_args(q, block_table, context_lens, max_context_len, out, lse_out, chunk_tokens,
-                     workspace, score, score_weight, pool=pool)
+                     workspace, score, score_weight, pool=pool, even_chunks=even_chunks)
     ws = workspace
     if ws is None:
         ws = allocate_workspace(pool, args, device=q.device)

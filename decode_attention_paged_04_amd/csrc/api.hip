@@ -31,6 +31,21 @@ constexpr int64_t kManyUnits = 256;
 constexpr int32_t kMinChunk = 1024;
 constexpr int32_t kChunkQuantum = 128;
 
+// Uneven chunk pairs.  Workgroup x runs on XCD x % 8, and on MI355X the odd
+// XCDs stream a few per cent slower than the even ones (per-workgroup
+// timestamps: mean finish 5-7 % later on long launches, the same XCDs on
+// every run and device measured).  An automatic split with an even number of
+// KV heads therefore pairs its chunks: in chunks 2p and 2p + 1 the heads of a
+// pair trade places, so the workgroup on the even XCD always takes the longer
+// chunk, C + d, and its neighbour on the odd XCD the shorter, C - d, with d
+// about 4.5 % of C in whole 32-token pairs (measured: 70B-shaped layer call
+// 320 -> 316 us, 256-request batch 421 -> 415 us, ragged batch 207 -> 205 us;
+// 8 % and more was slower again; a fused score was slower with it, so a call
+// with a score keeps even chunks, and so does a call with
+// KVD_FLAG_EVEN_CHUNKS, for batches whose shared blocks the L2 serves).  Unit boundaries stay fixed for given
+// arguments, so results stay deterministic.
+constexpr int32_t kSkewPermille = 45;
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Launch status is read back with hipGetLastError, which also reports an error
@@ -69,6 +84,7 @@ kvd_status plan_decode(const PoolView& p, const kvd_decode_args* a, DecodePlan* 
   if (a->n_q % p.n_kv != 0) return KVD_ERR_INVALID_ARG;
   if (a->n_q / p.n_kv > 16) return KVD_ERR_UNSUPPORTED;
   if (a->chunk_tokens < 0 || a->chunk_tokens % kvd::kBlock != 0) return KVD_ERR_INVALID_ARG;
+  if ((a->flags & ~KVD_FLAG_EVEN_CHUNKS) != 0) return KVD_ERR_INVALID_ARG;
   if (a->score && (a->score_stride < 1 || a->score_stride < a->max_context_len))
     return KVD_ERR_INVALID_ARG;
   // With a score every chunk must cover whole 32-token pairs: a pair's score
@@ -91,6 +107,12 @@ kvd_status plan_decode(const PoolView& p, const kvd_decode_args* a, DecodePlan* 
   if (chunk > whole) chunk = whole;
   pl.chunk = (int32_t)chunk;
   pl.n_chunks = (int32_t)std::max<int64_t>(1, (pl.ctx_bound + chunk - 1) / chunk);
+  pl.chunk_skew = 0;
+  if (a->chunk_tokens == 0 && pl.n_chunks >= 2 && p.n_kv % 2 == 0 && !a->score && pl.chunk % 32 == 0 &&
+      (a->flags & KVD_FLAG_EVEN_CHUNKS) == 0) {
+    const int32_t d = (int32_t)(((int64_t)pl.chunk * kSkewPermille + 16000) / 32000) * 32;
+    if (d > 0 && pl.chunk - d >= 32) pl.chunk_skew = d;
+  }
   // grids of 256-work-item workgroups: fewer than 2^32 work-items per launch
   if ((int64_t)pl.n_chunks * std::max(a->b, 1) * p.n_kv >= ((int64_t)1 << 24)) return KVD_ERR_UNSUPPORTED;
   if ((int64_t)a->b * a->n_q >= ((int64_t)1 << 24)) return KVD_ERR_UNSUPPORTED;
@@ -210,6 +232,7 @@ kvd_status decode_common(const kvd_pool* pool, int32_t layer, const kvd_decode_a
   L.ctx_bound = pl.ctx_bound;
   L.chunk = pl.chunk;
   L.n_chunks = pl.n_chunks;
+  L.chunk_skew = pl.chunk_skew;
   L.out = static_cast<uint16_t*>(a->out);
   L.lse_out = a->lse_out;
   if (external) {
@@ -454,6 +477,7 @@ kvd_status kvd_debug_unit_map(const kvd_pool* pool, const kvd_decode_args* args,
   L.ctx_bound = pl.ctx_bound;
   L.chunk = pl.chunk;
   L.n_chunks = pl.n_chunks;
+  L.chunk_skew = pl.chunk_skew;
   clear_stale_error();
   KVD_TRY_HIP(kvd::launch_debug_units(L, units, static_cast<hipStream_t>(hip_stream)));
   return KVD_OK;

@@ -239,6 +239,30 @@ __device__ inline Unit locate_unit(const DecodeLaunch& a, int k) {
   return Unit{-1, 0, 0};
 }
 
+// The KV head and token span [lo, hi) of chunk c for workgroup x.  Even
+// chunks: head x % n_kv, span [c*C, (c+1)*C).  With chunk_skew = d > 0 (an
+// even n_kv) the chunks 2p and 2p + 1 of a pair are C + d and C - d long for
+// an even head, C - d and C + d for an odd one, and the odd chunk of a pair
+// goes to the workgroup of the partner head (j ^ 1): the workgroup with x
+// even -- on an even XCD -- always takes the long chunk.  A last chunk
+// without a partner keeps [c*C, (c+1)*C).
+struct Span {
+  int j, lo, hi;
+};
+
+__device__ inline Span chunk_span(const DecodeLaunch& a, int x, int c) {
+  int j = x % a.n_kv;
+  int lo = c * a.chunk, hi = lo + a.chunk;
+  if (a.chunk_skew != 0 && (c | 1) < a.n_chunks) {
+    j ^= c & 1;
+    const int base = (c & ~1) * a.chunk;
+    const int mid = base + a.chunk + ((j & 1) == 0 ? a.chunk_skew : -a.chunk_skew);
+    lo = (c & 1) ? mid : base;
+    hi = (c & 1) ? base + 2 * a.chunk : mid;
+  }
+  return Span{j, lo, hi};
+}
+
 // KIND: kBf16 or kFp8 (one pool), or kMixed (a bf16 and an FP8 pool; each
 // table entry names its block's precision in kPrecisionBit -- the page
 // header).  A mixed kernel runs two passes, bf16 then FP8, each over the span
@@ -258,15 +282,16 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
   const int r16 = lane & 15;
 
   const int x = blockIdx.x;
-  const int j = x % a.n_kv;
   const Unit u = locate_unit(a, x / a.n_kv);
   // the unit is the same for every lane: keep it in scalar registers
   const int i = __builtin_amdgcn_readfirstlane(u.i);
   const int c = __builtin_amdgcn_readfirstlane(u.c);
   const int s = __builtin_amdgcn_readfirstlane(u.s);
   if (i < 0) return;                            // outside the grid's units (not reached)
-  const int lo = c * a.chunk;
-  const int ntok = min(s, lo + a.chunk) - lo;
+  const Span sp = chunk_span(a, x, c);
+  const int j = __builtin_amdgcn_readfirstlane(sp.j);
+  const int lo = __builtin_amdgcn_readfirstlane(sp.lo);
+  const int ntok = min(s, __builtin_amdgcn_readfirstlane(sp.hi)) - lo;
   const int g = a.g;
   const bool head_ok = r16 < g;
   const size_t ih = (size_t)i * a.n_q + (size_t)j * g + r16;   // this lane's head (when head_ok)
@@ -286,7 +311,7 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
   int32_t app_pid = -1;
   float app_sK = 0.f, app_sV = 0.f;
   if constexpr (!MIX) {
-    if (a.new_k != nullptr && s > 0 && (s - 1) / a.chunk == c && load_invariant(a.context_lens + i) == s) {
+    if (a.new_k != nullptr && s > 0 && s - 1 >= lo && s - 1 < lo + ntok && load_invariant(a.context_lens + i) == s) {
       const int tl = s - 1;
       const int32_t pid = load_invariant(a.block_table + (size_t)i * a.max_blocks + tl / kBlock);
       if (pid >= 0 && pid < a.num_blocks) {
@@ -646,16 +671,21 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
 }
 
 // Test hook: the unit each workgroup of a decode launch with these arguments
-// takes -- out[3x .. 3x+2] = (sequence, chunk, clamped context length) of
-// workgroup x, whose KV head is x % n_kv.  One wave per workgroup runs
-// locate_unit exactly as the decode kernels do.
+// takes -- out[6x .. 6x+5] = (sequence, chunk, clamped context length, KV
+// head, first token, end token of the chunk) of workgroup x.  One wave per
+// workgroup runs locate_unit and chunk_span exactly as the decode kernels do.
 __global__ __launch_bounds__(64) void debug_units_kernel(DecodeLaunch a, int32_t* __restrict__ out) {
   const int x = blockIdx.x;
   const Unit u = locate_unit(a, x / a.n_kv);
+  const Span sp = chunk_span(a, x, u.c);
   if (threadIdx.x == 0) {
-    out[3 * (size_t)x] = u.i;
-    out[3 * (size_t)x + 1] = u.c;
-    out[3 * (size_t)x + 2] = u.s;
+    int32_t* o = out + 6 * (size_t)x;
+    o[0] = u.i;
+    o[1] = u.c;
+    o[2] = u.s;
+    o[3] = sp.j;
+    o[4] = sp.lo;
+    o[5] = sp.hi;
   }
 }
 

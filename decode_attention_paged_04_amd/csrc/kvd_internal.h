@@ -27,6 +27,7 @@ struct DecodePlan {
   int32_t n_chunks;         // chunks per sequence at max_context_len
   int32_t ctx_bound;        // clamp for every s_i
   int32_t logit_stride;     // row length of the logit scratch (scores only)
+  int32_t chunk_skew;       // tokens that pass from the odd to the even chunk of a pair
   bool final_direct;        // one chunk: no partials, the workgroup writes out/lse itself
   bool scores;
   size_t off_part_o, off_part_lse, off_logits, off_lse2, total;
@@ -46,6 +47,7 @@ struct DecodeLaunch {
   const int32_t* block_table;
   const int32_t* context_lens;
   int32_t b, n_q, n_kv, g, max_blocks, num_blocks, ctx_bound, chunk, n_chunks;
+  int32_t chunk_skew;       // 0, or d of the uneven chunk pairs (chunk_span)
   // outputs: either final (out/lse_out) or partials
   uint16_t* out;
   float* lse_out;

@@ -112,6 +112,7 @@ def _args(**kw):
     (dict(chunk_tokens=16, workspace=FAKE + 16, workspace_bytes=1 << 30), 4),   # misaligned
     (dict(q=FAKE + 8), 1), (dict(out=FAKE + 4), 1),                            # misaligned vectors
     (dict(lse_out=FAKE + 2), 1), (dict(score=FAKE + 2, score_stride=100), 1),
+    (dict(flags=2), 1), (dict(flags=1 << 31), 1),                            # unknown flag bits
 ])
 def test_decode_argument_errors(kw, status):
     pool = _pool()

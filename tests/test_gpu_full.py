@@ -158,14 +158,17 @@ def test_full_shared_prefix_batch(env, name, chunks):
         Ki = torch.cat([Kc[:P], Kc[a:e]]) if i else Kc[a:e]
         Vi = torch.cat([Vc[:P], Vc[a:e]]) if i else Vc[a:e]
         refs[i] = attention.decode_sequence(qf[i], H.bf16_to_f64(Ki), H.bf16_to_f64(Vi))
-    for chunk in chunks:
+    # the automatic split as the benchmark runs it (even chunks: the batch shares
+    # its prompt) and with the default uneven chunk pairs
+    for chunk, even in [(c, e) for c in chunks for e in ((True, False) if c == 0 else (False,))]:
         out = torch.empty_like(q)
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
-        kvd.decode(pool, 0, q, table_t, lens_t, int(lens.max()), out=out, lse_out=lse, chunk_tokens=chunk)
+        kvd.decode(pool, 0, q, table_t, lens_t, int(lens.max()), out=out, lse_out=lse, chunk_tokens=chunk,
+                   even_chunks=even)
         torch.cuda.synchronize()
         for i in sample:
             ref_o, ref_l = refs[i]
-            mx, rel = H.assert_bf16_close(out[i], ref_o, what=f"{name} chunk {chunk} seq {i}")
-            H.say(f"{name} chunk {chunk} seq {i}: max-abs {mx:.2e} rel-L2 {rel:.2e}")
+            mx, rel = H.assert_bf16_close(out[i], ref_o, what=f"{name} chunk {chunk} even {even} seq {i}")
+            H.say(f"{name} chunk {chunk} even {even} seq {i}: max-abs {mx:.2e} rel-L2 {rel:.2e}")
             H.assert_lse_close(lse[i:i + 1], ref_l[None])
         assert not torch.isnan(out.float()).any()

@@ -10,6 +10,13 @@ the other two runs sequence by sequence.  The order only decides which
 workgroup computes a unit; the batch sizes here reach every branch of the
 location code (one sequence per lane, up to eight, more than eight, more than
 64 per lane; more than 64 chunks).
+
+Each workgroup also reports its KV head and token span.  They must follow the
+documented split: head x % n_kv and span [c*C, (c+1)*C), or, for an automatic
+split with an even n_kv and two or more chunks, the uneven pairs (C + d on the
+workgroups with x even, C - d on their neighbours, d = 32 * floor((45 C +
+16000) / 32000)); and for every sequence and head the spans of its chunks
+must tile [0, n_chunks * C) exactly.
 """
 import numpy as np
 import pytest
@@ -36,7 +43,43 @@ def expected_order(lens, chunk, n_chunks, bound):
     return full + part + empty, s
 
 
-def _case(kvd, torch, lens, n_kv, chunk, max_ctx, g=2, d=64):
+def expected_span(x, c, n_kv, C, nc, skew):
+    """(head, first token, end token) of chunk c for workgroup x, from the rule above."""
+    j = x % n_kv
+    if skew and (c | 1) < nc:
+        j ^= c & 1
+        base = (c & ~1) * C
+        mid = base + C + (skew if j % 2 == 0 else -skew)
+        return (j, mid, base + 2 * C) if c & 1 else (j, base, mid)
+    return j, c * C, (c + 1) * C
+
+
+def expected_skew(chunk_arg, C, nc, n_kv):
+    if chunk_arg != 0 or nc < 2 or n_kv % 2 or C % 32:
+        return 0
+    d = 32 * ((45 * C + 16000) // 32000)
+    return d if d > 0 and C - d >= 32 else 0
+
+
+def _check_spans(units, n_kv, C, nc, skew):
+    b_units = units.shape[0]
+    for x in range(b_units):
+        i, c, s, j, lo, hi = (int(v) for v in units[x])
+        assert (j, lo, hi) == expected_span(x, c, n_kv, C, nc, skew), (x, units[x])
+        if skew and (c | 1) < nc:
+            assert hi - lo == (C + skew if x % 2 == 0 else C - skew), (x, units[x])
+    # per (sequence, head): the spans tile [0, nc * C)
+    spans = {}
+    for i, c, s, j, lo, hi in units.tolist():
+        spans.setdefault((i, j), []).append((c, lo, hi))
+    for key, v in spans.items():
+        v.sort()
+        assert [c for c, _, _ in v] == list(range(nc)), key
+        assert v[0][1] == 0 and v[-1][2] == nc * C, key
+        assert all(v[k][2] == v[k + 1][1] for k in range(nc - 1)), key
+
+
+def _case(kvd, torch, lens, n_kv, chunk, max_ctx, g=2, d=64, even=False):
     b = len(lens)
     pool = kvd.allocate_pool(1, 1, n_kv, d)
     mb = max(1, -(-max_ctx // 16))
@@ -44,7 +87,7 @@ def _case(kvd, torch, lens, n_kv, chunk, max_ctx, g=2, d=64):
     table = torch.zeros((b, mb), dtype=torch.int32, device="cuda")
     lens_t = torch.tensor(np.asarray(lens, dtype=np.int32), device="cuda")
     out = torch.empty_like(q)
-    args = kvd.make_args(q, table, lens_t, max_ctx, out, chunk_tokens=chunk, pool=pool)
+    args = kvd.make_args(q, table, lens_t, max_ctx, out, chunk_tokens=chunk, pool=pool, even_chunks=even)
     ch, nc = kvd.kvd_decode_plan(pool, args)
     units = kvd.kvd_debug_unit_map(pool, args).cpu().numpy()
     return units, ch, nc
@@ -52,9 +95,9 @@ def _case(kvd, torch, lens, n_kv, chunk, max_ctx, g=2, d=64):
 
 def _check(units, lens, n_kv, chunk, n_chunks, bound):
     order, s = expected_order(lens, chunk, n_chunks, bound)
-    assert units.shape == (len(lens) * n_kv * n_chunks, 3)
+    assert units.shape == (len(lens) * n_kv * n_chunks, 6)
     for j in range(n_kv):
-        got = units[j::n_kv]
+        got = units[j::n_kv, :3]
         assert got.shape[0] == len(order)
         exp = np.array(order, dtype=np.int64).reshape(-1, 2)
         bad = np.nonzero((got[:, 0] != exp[:, 0]) | (got[:, 1] != exp[:, 1]))[0]
@@ -78,6 +121,12 @@ CASES = [
     ("4200 seqs (more than 64 per lane)", 4200, (0, 200), 2, 16, 200),
     ("9000 seqs", 9000, (0, 100), 1, 32, 100),
     ("lengths above the bound", 100, (0, 5000), 1, 256, 3000),
+    # automatic splits: uneven pairs (32 chunks; 2 chunks; 5 chunks, the last
+    # without a partner), and none with an odd n_kv
+    ("auto, one sequence, 8 heads", 1, (40000, 40000), 8, 0, 40000),
+    ("auto, 64 seqs", 64, (0, 5000), 2, 0, 5000),
+    ("auto, odd chunk count", 3, (1000, 5000), 2, 0, 5000),
+    ("auto, one KV head", 2, (1000, 5000), 1, 0, 5000),
 ]
 
 
@@ -91,3 +140,15 @@ def test_unit_map_is_the_promised_order(env, name, b, rng_lens, n_kv, chunk, max
         lens[0], lens[1], lens[2] = 0, 1, min(max_ctx, 16 * (max(chunk, 16) // 16) * 2)
     units, ch, nc = _case(kvd, torch, lens, n_kv, chunk, max_ctx)
     _check(units, lens, n_kv, ch, nc, min(max_ctx, 16 * max(1, -(-max_ctx // 16))))
+    _check_spans(units, n_kv, ch, nc, expected_skew(chunk, ch, nc, n_kv))
+
+
+def test_even_chunks_flag_keeps_even_spans(env):
+    """KVD_FLAG_EVEN_CHUNKS: an automatic split that would pair its chunks
+    unevenly keeps [c*C, (c+1)*C) and head x % n_kv for every workgroup."""
+    kvd, torch = env
+    lens = np.full(3, 5000)
+    units, ch, nc = _case(kvd, torch, lens, 2, 0, 5000, even=True)
+    assert nc == 5 and expected_skew(0, ch, nc, 2) > 0          # uneven without the flag
+    _check(units, lens, 2, ch, nc, 5000)
+    _check_spans(units, 2, ch, nc, 0)
