@@ -67,14 +67,18 @@ __device__ inline int qk_channel0(int c, int G) { return 32 * c + 8 * G; }
 // Launch order of the (sequence, chunk) units.  Per KV head the grid holds
 // b * n_chunks units, n_chunks covering the longest allowed context, but a
 // sequence of s tokens fills only ceil(s / chunk) of its chunks.  Workgroup x
-// takes KV head x % n_kv and unit k = x / n_kv of this order, in three runs:
+// takes unit k = x / n_kv of this order (and the KV head and span chunk_span
+// gives it), in three runs:
 // the full chunks chunk-major (chunk 0 of every sequence that has it, in
 // sequence order, then chunk 1, ...), then the partly filled last chunks, then
 // the empty chunks, sequence by sequence.  The hardware hands out workgroups in grid
 // order, so the shorter units run last and the final workgroups drain sooner;
 // an empty chunk only marks itself empty for the merge (or writes a zero
 // output), and at the end of the grid such workgroups no longer hold compute
-// units while chunks with tokens wait.
+// units while chunks with tokens wait.  The runs are counted with even chunks
+// of C tokens; with uneven chunk pairs a chunk near a sequence's end may hold a
+// few more or fewer tokens than that count says, which moves work between the
+// runs but never changes which tokens a unit covers.
 // Each wave finds its unit itself, in two rounds of loads whatever b is: lane
 // l owns sequences [l per, (l + 1) per), per = ceil(b / 64), and counts their
 // chunks of each kind (its loads are independent of one another); a prefix
