@@ -6,8 +6,10 @@ on the KV head's parity (kvd_decode_plan documents the spans).  The per-chunk
 partials must equal the oracle's attention over exactly those spans, their
 merge the one-call step bit for bit and the oracle's step within tolerance; a
 fused append whose token lies where the two parities' spans differ must store
-it once, before it is read, exactly as kvd_write_kv does; and a last chunk
-without a partner keeps its even span.
+it once, before it is read, exactly as kvd_write_kv does; dropped blocks at the
+pair boundaries must leave exactly the kept tokens attended; and a last chunk
+without a partner keeps its even span.  (The mixed-precision decode over such
+pairs is checked with the other mixed tests.)
 """
 import numpy as np
 import pytest
@@ -133,3 +135,36 @@ def test_fused_append_into_uneven_pairs(env, fp8):
     if fp8:
         assert torch.equal(ref_pool.scales.view(torch.int32), fused_pool.scales.view(torch.int32))
     assert not torch.equal(case.pool.kv, fused_pool.kv)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_restricted_decode_over_uneven_pairs(env, fp8):
+    """Dropped blocks (negative table entries) inside chunks of uneven length:
+    the step attends to exactly the kept tokens, as the oracle's restricted step."""
+    kvd, H, W, torch = env
+    from oracle import tiers
+    case = _case(H, W, fp8, 98 + int(fp8))
+    rng = np.random.default_rng(99)
+    table = case.table.copy()
+    for i, s in enumerate(LENS):
+        nb = -(-s // 16)
+        for b in range(nb):
+            if rng.random() < 0.3:
+                table[i, b] = -1
+    # blocks at the pair boundaries of both head parities (tokens 992-1055 and 3040-3103)
+    table[0, 62:66] = -1
+    table[1, 190:194] = -1
+    qf = H.bf16_to_f64(case.q[0])
+    ref_o = np.zeros(qf.shape)
+    ref_l = np.zeros(qf.shape[:2])
+    for i, s in enumerate(LENS):
+        K, V = case.logical(0, i)
+        keep = np.array([table[i, t // 16] >= 0 for t in range(s)], dtype=bool)
+        ref_o[i], ref_l[i] = tiers.restricted_decode(qf[i], K, V, keep)
+    out = torch.empty_like(case.q[0])
+    lse = torch.empty(case.q[0].shape[:2], dtype=torch.float32, device="cuda")
+    kvd.decode(case.pool, 0, case.q[0], torch.from_numpy(table).cuda(), case.lens_t, case.max_ctx,
+               out=out, lse_out=lse, chunk_tokens=0)
+    torch.cuda.synchronize()
+    H.assert_bf16_close(out, ref_o, what=f"restricted over uneven pairs fp8={fp8}")
+    H.assert_lse_close(lse, ref_l)

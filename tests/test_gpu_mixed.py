@@ -27,14 +27,14 @@ def env():
 class MixedCase:
     """Two pools, the sequences' data, and the oracle's view of every block."""
 
-    def __init__(self, kvd, H, torch, d, seed, mode="random"):
+    def __init__(self, kvd, H, torch, d, seed, mode="random", lens=LENS):
         rng = np.random.default_rng(seed)
         g = torch.Generator().manual_seed(seed)
         self.d = d
-        self.lens = LENS
+        self.lens = lens = list(lens)
         blocks16, blocks8 = [], []                       # (seq, logical block)
         self.prec = []
-        for i, s in enumerate(LENS):
+        for i, s in enumerate(lens):
             nb = -(-s // 16)
             if mode == "bf16":
                 p = [0] * nb
@@ -57,12 +57,12 @@ class MixedCase:
             self.phys[key] = int(phys16[k])
         for k, key in enumerate(blocks8):
             self.phys[key] = int(phys8[k])
-        self.K = [torch.randn((s, N_KV, d), generator=g).to(torch.bfloat16) for s in LENS]
-        self.V = [torch.randn((s, N_KV, d), generator=g).to(torch.bfloat16) for s in LENS]
-        self.q = torch.randn((len(LENS), N_KV * G, d), generator=g).to(torch.bfloat16)
+        self.K = [torch.randn((s, N_KV, d), generator=g).to(torch.bfloat16) for s in lens]
+        self.V = [torch.randn((s, N_KV, d), generator=g).to(torch.bfloat16) for s in lens]
+        self.q = torch.randn((len(lens), N_KV * G, d), generator=g).to(torch.bfloat16)
         for pool, which in ((self.pool16, 0), (self.pool8, 1)):
             Ks, Vs, slots = [], [], []
-            for i, s in enumerate(LENS):
+            for i, s in enumerate(lens):
                 for b in range(-(-s // 16)):
                     if self.prec[i][b] != which:
                         continue
@@ -75,7 +75,7 @@ class MixedCase:
                                  torch.tensor(slots, dtype=torch.int32, device="cuda"))
         # rows (the partial last block, if any, is the last of its run)
         rows, self.ctx = [], []
-        for i, s in enumerate(LENS):
+        for i, s in enumerate(lens):
             nb = -(-s // 16)
             ids16 = [self.phys[(i, b)] for b in range(nb) if not self.prec[i][b]]
             ids8 = [self.phys[(i, b)] for b in range(nb) if self.prec[i][b]]
@@ -85,7 +85,7 @@ class MixedCase:
             rows.append(row)
             self.ctx.append(c)
         self.mb = max(max(len(r) for r in rows), 1)
-        self.table = np.full((len(LENS), self.mb), -1, dtype=np.int32)
+        self.table = np.full((len(lens), self.mb), -1, dtype=np.int32)
         for i, r in enumerate(rows):
             self.table[i, :len(r)] = r
         self.H = H
@@ -114,6 +114,30 @@ class MixedCase:
                          max(max(self.ctx), 1), out=out, lse_out=lse, chunk_tokens=chunk)
         torch.cuda.synchronize()
         return out, lse
+
+
+# Lengths whose automatic split at a 5,000-token bound is five 1,024-token
+# chunks with uneven pairs (d = 32): the two passes then step over the spans of
+# chunks whose boundaries depend on the KV head's parity.
+PAIR_LENS = [5000, 3050, 1025, 0, 2049]
+
+
+def test_mixed_decode_over_uneven_chunk_pairs(env):
+    kvd, H, torch = env
+    from oracle import mixed
+    case = MixedCase(kvd, H, torch, 128, seed=760, lens=PAIR_LENS)
+    args = kvd.make_args(case.q.cuda(), torch.from_numpy(case.table).cuda(),
+                         torch.tensor(case.ctx, dtype=torch.int32, device="cuda"), max(case.ctx),
+                         torch.empty_like(case.q).cuda(), pool=case.pool16)
+    assert kvd.kvd_decode_plan(case.pool16, args) == (1024, 5)
+    qf = H.bf16_to_f64(case.q)
+    ref_o = np.zeros(qf.shape)
+    ref_l = np.zeros(qf.shape[:2])
+    for i in range(len(PAIR_LENS)):
+        ref_o[i], ref_l[i] = mixed.decode_mixed(qf[i], [(k, v) for k, v, _ in case.stored_blocks(i)])
+    out, lse = case.run(kvd, torch, case.table, 0)
+    H.assert_bf16_close(out, ref_o, what="mixed over uneven chunk pairs")
+    H.assert_lse_close(lse, ref_l)
 
 
 @pytest.mark.parametrize("d", [64, 128])
