@@ -624,7 +624,8 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
 
-  // Combine the waves: common max, rescaled sums and outputs.
+  // Combine the waves after one barrier: each wave leaves its max, sum and
+  // unscaled output; the readers take the common max and rescale.
   __shared__ float sh_m[kWaves][16];
   __shared__ float sh_l[kWaves][16];
   __shared__ f32x4 sh_o[kWaves][NM][64];
@@ -632,27 +633,27 @@ __global__ __launch_bounds__(64 * kWaves, KIND == kFp8 ? 3 : 2) void decode_kern
     sh_m[wave][r16] = m;
     sh_l[wave][r16] = l;
   }
+#pragma unroll
+  for (int mm = 0; mm < NM; ++mm) sh_o[wave][mm][lane] = o[mm];
   __syncthreads();
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh_m[w][r16]);
+  float fw[kWaves];
   float L = 0.f;
-  if (M != -INFINITY) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) L += sh_l[w][r16] * __builtin_amdgcn_exp2f(sh_m[w][r16] - M);
+  for (int w = 0; w < kWaves; ++w) {
+    fw[w] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sh_m[w][r16] - M);
+    L += sh_l[w][r16] * fw[w];
   }
-  const float f_own = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-#pragma unroll
-  for (int mm = 0; mm < NM; ++mm) sh_o[wave][mm][lane] = o[mm] * f_own;
-  __syncthreads();
 
   const bool empty = !(L > 0.f);
   const float inv_l = empty ? 0.f : 1.0f / L;
   const float lse2 = empty ? -INFINITY : M + __log2f(L);
   for (int mm = wave; mm < NM; mm += kWaves) {
-    f32x4 acc = sh_o[0][mm][lane];
+    f32x4 acc = sh_o[0][mm][lane] * fw[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) acc += sh_o[w][mm][lane];
+    for (int w = 1; w < kWaves; ++w) acc += sh_o[w][mm][lane] * fw[w];
     acc *= inv_l;
     if (!head_ok) continue;
     const int ch = 16 * mm + 4 * G;
