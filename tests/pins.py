@@ -207,6 +207,44 @@ def split_merge_max_error(seed=3) -> float:
     return worst
 
 
+def uneven_split_merge_max_error(seed=5) -> float:
+    """Merging the partials of any contiguous spans that tile the context --
+    random cut points, and chunks paired as C + d, C - d (or C - d, C + d) with a
+    last chunk left alone -- reproduces the unsplit result."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((8, 32))
+    s = 1000
+    K = rng.standard_normal((s, 2, 32)) * 2
+    V = rng.standard_normal((s, 2, 32))
+    o, lse = attention.decode_sequence(q, K, V)
+
+    def merged(bounds):
+        spans = list(zip(bounds[:-1], bounds[1:]))
+        oc = np.zeros((q.shape[0], len(spans), q.shape[1]))
+        lc = np.full((q.shape[0], len(spans)), -np.inf)
+        for c, (lo, hi) in enumerate(spans):
+            if lo < hi:
+                oc[:, c], lc[:, c] = attention.decode_sequence(q, K[lo:hi], V[lo:hi])
+        return attention.merge_partials(oc, lc)
+
+    cases = []
+    for _ in range(4):
+        cuts = np.sort(rng.choice(np.arange(1, s), size=int(rng.integers(1, 12)), replace=False))
+        cases.append([0, *cuts.tolist(), s])
+    C, d = 224, 32                                   # 5 chunks at C: pairs (0, 1), (2, 3), chunk 4
+    for sign in (1, -1):
+        b = [0]
+        for c in range(5):
+            base = (c & ~1) * C
+            b.append(min(s, base + C + sign * d if c % 2 == 0 and c + 1 < 5 else (c + 1) * C))
+        cases.append(b)
+    worst = 0.0
+    for bounds in cases:
+        om, lm = merged(bounds)
+        worst = max(worst, float(np.max(np.abs(om - o))), float(np.max(np.abs(lm - lse))))
+    return worst
+
+
 def special_case_failures(seed=4) -> list:
     rng = np.random.default_rng(seed)
     bad = []

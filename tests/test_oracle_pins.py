@@ -71,6 +71,10 @@ def test_split_and_merge_is_exact():
     assert pins.split_merge_max_error() < 1e-12
 
 
+def test_uneven_spans_merge_exactly():
+    assert pins.uneven_split_merge_max_error() < 1e-12
+
+
 def test_merge_edge_cases():
     rng = np.random.default_rng(11)
     oc = rng.standard_normal((3, 4, 8))
