@@ -50,7 +50,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Launch status is read back with hipGetLastError, which also reports an error
 // left behind by an earlier, unrelated runtime call in this thread; clear that
-// first so that only this call's launches are judged.
+// first so that only this call's launches are checked.
 void clear_stale_error() { (void)hipGetLastError(); }
 
 // HIP error behind the calling thread's most recent KVD_ERR_HIP (errno-like).
