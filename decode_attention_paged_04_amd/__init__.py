@@ -354,13 +354,13 @@ def kvd_decode_attn_mixed(pool_bf16: Pool, pool_fp8: Pool, layer: int, args: Dec
 
 def decode_mixed(pool_bf16: Pool, pool_fp8: Pool, layer: int, q, block_table, context_lens,
                  max_context_len: int, out=None, lse_out=None, chunk_tokens: int = 0, workspace=None,
-                 stream=None):
+                 stream=None, even_chunks: bool = False):
     """Convenience: allocate out/workspace as needed and run one mixed-precision decode."""
     import torch
     if out is None:
         out = torch.empty_like(q)
     args = make_args(q, block_table, context_lens, max_context_len, out, lse_out, chunk_tokens,
-                     workspace, pool=pool_bf16)
+                     workspace, pool=pool_bf16, even_chunks=even_chunks)
     ws = workspace if workspace is not None else allocate_workspace(pool_bf16, args, device=q.device)
     kvd_decode_attn_mixed(pool_bf16, pool_fp8, layer, args, stream)
     return out, ws
